@@ -1,0 +1,283 @@
+"""CPU oracle for tree-causal attention and greedy tree acceptance (fp64).
+
+TEST INFRASTRUCTURE. This module is the checker, not the product: only the
+test suite, the smoke check and the benchmark's CPU-baseline leg may import
+it. The HIP library never calls it, and it shares no code with the library.
+
+Source of the definitions: "JetFlow: Breaking the Scaling Ceiling of
+Speculative Decoding with Parallel Tree Drafting", the gist.science pages
+(Japanese and German technical summaries).
+  * Section 2 (method), tree-causal attention mask: every node of the draft
+    tree attends to the input prefix and to its own ancestors in the tree, and
+    never to its descendants or to unrelated sibling branches. The branch
+    factorisation printed there conditions each node only on its own
+    root-to-node path; we read the path as including the node itself, so a
+    chain-shaped tree reduces to ordinary causal attention.
+  * Section 3 (contributions): the tree is verified by the target model over
+    a paged KV cache.
+  * Lay summary and the qxai.app commentary: the target accepts the drafted
+    tokens up to the point where it disagrees.
+
+Everything the pages leave open is resolved by the plainest reading:
+  - node order is topological: parent[0] = -1 and 0 <= parent[i] < i;
+  - query head h reads KV head h // (Hq // Hkv);
+  - scores are sm_scale * q.k, softmax over the visible keys, output = P V,
+    log-sum-exp in natural log;
+  - node 0 is the last committed token (always accepted); a child c agrees
+    when its draft token equals the target's choice at its parent; the
+    accepted path is the longest root-to-node path on which every node
+    agrees, ties to the smallest end-node index; the bonus token is the
+    target's choice at the end of that path;
+  - the target's choice at a node is the first index of the largest logit;
+    NaN never wins; a row of NaN only yields 0.
+
+Arithmetic is fp64 throughout. Inputs stored in bf16 or fp32 are widened
+exactly, so the oracle sees the same rounded values the GPU sees.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+ANC_WORDS = 4          # the ancestor bitset is 4 x 64 bits per node
+MAX_NODES = 64 * ANC_WORDS
+
+
+def _f64(x) -> np.ndarray:
+    """Widen a torch tensor (any float dtype) or array to float64 exactly."""
+    if hasattr(x, "detach"):
+        import torch
+        return x.detach().to("cpu").to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        return x.detach().to("cpu").numpy().astype(np.int64)
+    return np.asarray(x, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Tree structure (section 2, tree-causal attention mask)
+# --------------------------------------------------------------------------
+
+def is_valid_tree(parent: Sequence[int]) -> bool:
+    """A draft tree in creation order: one root at index 0, every other node's
+    parent created before it."""
+    p = [int(x) for x in parent]
+    if len(p) == 0 or len(p) > MAX_NODES:
+        return False
+    if p[0] != -1:
+        return False
+    return all(0 <= p[i] < i for i in range(1, len(p)))
+
+
+def root_path(parent: Sequence[int], v: int) -> list:
+    """Nodes on the path from the root to v, root first, v last (naive walk
+    up the parent pointers). Requires a valid tree."""
+    path = []
+    u = int(v)
+    while u != -1:
+        path.append(u)
+        u = int(parent[u])
+    path.reverse()
+    return path
+
+
+def ancestor_matrix(parent: Sequence[int]) -> np.ndarray:
+    """Dense visibility among tree nodes: A[i, j] is True iff node j is on
+    the root-to-i path (j == i included). Requires a valid tree."""
+    n = len(parent)
+    A = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in root_path(parent, i):
+            A[i, j] = True
+    return A
+
+
+def pack_bitset(A: np.ndarray) -> np.ndarray:
+    """Encode each row of A as 4 little-endian 64-bit words: node j is bit
+    (j % 64) of word (j // 64). Bits at or beyond N are zero."""
+    n = A.shape[0]
+    words = np.zeros((n, ANC_WORDS), dtype=np.uint64)
+    for i in range(n):
+        for j in range(n):
+            if A[i, j]:
+                words[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return words
+
+
+def build_ancestor_mask(parent) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Batched mask builder: parent int[B, N] ->
+    (anc uint64[B, N, 4], depth int32[B, N], bad_tree int32[B]).
+
+    depth counts the nodes on the root-to-node path (root = 1). For a
+    sequence whose parent array is not a valid tree only bad_tree (= 1) is
+    defined; its anc/depth rows are left zero here."""
+    P = _i64(parent)
+    B, N = P.shape
+    anc = np.zeros((B, N, ANC_WORDS), dtype=np.uint64)
+    depth = np.zeros((B, N), dtype=np.int32)
+    bad = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        if not is_valid_tree(P[b]):
+            bad[b] = 1
+            continue
+        A = ancestor_matrix(P[b])
+        anc[b] = pack_bitset(A)
+        depth[b] = A.sum(axis=1).astype(np.int32)
+    return anc, depth, bad
+
+
+# --------------------------------------------------------------------------
+# Paged prefix (section 3: verification over a paged KV cache)
+# --------------------------------------------------------------------------
+
+def gather_prefix(pages: np.ndarray, table_row: np.ndarray, L: int, page_size: int) -> np.ndarray:
+    """Prefix token t of a sequence lives in slot t % page_size of page
+    table_row[t // page_size]; pages is [P, Hkv, page_size, D].
+    Returns [L, Hkv, D]."""
+    Hkv, D = pages.shape[1], pages.shape[3]
+    out = np.empty((L, Hkv, D), dtype=np.float64)
+    for t in range(L):
+        out[t] = pages[int(table_row[t // page_size]), :, t % page_size, :]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Tree-causal attention (section 2 mask, section 3 paged verification)
+# --------------------------------------------------------------------------
+
+def _softmax_attend(qrows: np.ndarray, K: np.ndarray, V: np.ndarray, visible: np.ndarray,
+                    sm_scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Masked attention of a few query rows over explicit keys.
+    qrows [n, D], K/V [T, D], visible bool [n, T] -> (O [n, D], lse [n])."""
+    s = sm_scale * (qrows @ K.T)
+    s = np.where(visible, s, -np.inf)
+    rowmax = s.max(axis=1, keepdims=True)
+    e = np.exp(s - rowmax)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    return p @ V, rowmax[:, 0] + np.log(z[:, 0])
+
+
+def _sequence_keys(b, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, page_size):
+    L = int(prefix_len[b])
+    Kp = gather_prefix(k_pages, block_table[b], L, page_size)
+    Vp = gather_prefix(v_pages, block_table[b], L, page_size)
+    K = np.concatenate([Kp, k_tree[b]], axis=0)   # [L + N, Hkv, D]
+    V = np.concatenate([Vp, v_tree[b]], axis=0)
+    return L, K, V
+
+
+def tree_attention(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, parent,
+                   sm_scale: Optional[float] = None, page_size: int = 16,
+                   rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Tree-causal attention.
+
+    q [B, N, Hq, D]; k_pages/v_pages [P, Hkv, page, D]; block_table int[B, *];
+    prefix_len int[B]; k_tree/v_tree [B, N, Hkv, D]; parent int[B, N].
+
+    Node i of sequence b sees keys 0..L_b-1 of its prefix and the tree keys of
+    the nodes on its root-to-i path (itself included) -- an explicit dense
+    [N, L_b + N] mask per sequence. Returns (out float64 [B, N, Hq, D],
+    lse float64 [B, N, Hq]). With `rows` = iterable of (b, node, head), only
+    those entries are computed; the others stay NaN.
+    """
+    Q = _f64(q)
+    KP, VP = _f64(k_pages), _f64(v_pages)
+    KT, VT = _f64(k_tree), _f64(v_tree)
+    BT, PL, PAR = _i64(block_table), _i64(prefix_len), _i64(parent)
+    B, N, Hq, D = Q.shape
+    Hkv = KP.shape[1]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.full((B, N, Hq, D), np.nan)
+    lse = np.full((B, N, Hq), np.nan)
+    if rows is None:
+        want = {(b, h): list(range(N)) for b in range(B) for h in range(Hq)}
+    else:
+        want = {}
+        for (b, n, h) in rows:
+            want.setdefault((int(b), int(h)), []).append(int(n))
+    by_seq = {}
+    for (b, h), nodes in want.items():
+        by_seq.setdefault(b, []).append((h, nodes))
+    for b, heads in by_seq.items():
+        if not is_valid_tree(PAR[b]):
+            raise ValueError(f"sequence {b}: parent array is not a valid tree")
+        L, K, V = _sequence_keys(b, KP, VP, BT, PL, KT, VT, page_size)
+        A = ancestor_matrix(PAR[b])
+        mask = np.zeros((N, L + N), dtype=bool)
+        mask[:, :L] = True
+        mask[:, L:] = A
+        for h, nodes in heads:
+            g = h // G
+            idx = np.asarray(sorted(set(nodes)))
+            o, l = _softmax_attend(Q[b, idx, h, :], K[:, g, :], V[:, g, :], mask[idx], sm_scale)
+            out[b, idx, h, :] = o
+            lse[b, idx, h] = l
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Target choice and greedy acceptance (lay summary; qxai.app commentary)
+# --------------------------------------------------------------------------
+
+def argmax_first(row) -> int:
+    """Index of the largest value, the first one among equal maxima
+    (-0 and +0 are equal). NaN never wins; a row of only NaN yields 0."""
+    x = _f64(row).reshape(-1)
+    ok = ~np.isnan(x)
+    if not ok.any():
+        return 0
+    best = x[ok].max()
+    return int(np.nonzero(ok & (x == best))[0][0])
+
+
+def target_choice(logits) -> np.ndarray:
+    """logits [B, N, V] -> int32 [B, N], one argmax_first per row."""
+    X = _f64(logits)
+    B, N, _ = X.shape
+    out = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for v in range(N):
+            out[b, v] = argmax_first(X[b, v])
+    return out
+
+
+def accept_one(parent: Sequence[int], draft: Sequence[int], next_tok: Sequence[int]):
+    """Greedy acceptance for one tree, by a naive walk of every node's path.
+
+    Returns (accept_len, accepted_nodes list padded with -1 to N, bonus)."""
+    N = len(parent)
+    best_v, best_len = 0, 1
+    for v in range(N):
+        path = root_path(parent, v)
+        agrees = all(int(draft[u]) == int(next_tok[int(parent[u])]) for u in path[1:])
+        if agrees and len(path) > best_len:
+            best_v, best_len = v, len(path)
+    path = root_path(parent, best_v)
+    nodes = path + [-1] * (N - len(path))
+    return len(path) - 1, nodes, int(next_tok[best_v])
+
+
+def tree_accept(parent, draft, next_tokens):
+    """Batched acceptance: parent/draft/next_tokens int[B, N] ->
+    (accept_len int32[B], accepted_nodes int32[B, N], bonus int32[B])."""
+    P, Dr, Nx = _i64(parent), _i64(draft), _i64(next_tokens)
+    B, N = P.shape
+    alen = np.zeros(B, dtype=np.int32)
+    nodes = np.full((B, N), -1, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        if not is_valid_tree(P[b]):
+            raise ValueError(f"sequence {b}: parent array is not a valid tree")
+        a, nd, bo = accept_one(P[b], Dr[b], Nx[b])
+        alen[b], nodes[b], bonus[b] = a, nd, bo
+    return alen, nodes, bonus
