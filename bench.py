@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the budget-16 workload
+(Qwen3-8B attention layer: 32 query / 8 KV heads, head dim 128, bf16, prefix
+2048 in shuffled 16-token pages, a 16-node chain tree):
+    jf_build_ancestor_mask -> jf_tree_attention -> jf_tree_accept (argmax over
+    bf16 target logits [1, 16, 151936], then the acceptance walk).
+Steps are replayed from HIP graphs (one captured step per input set); the
+input sets rotate through more than twice the 256 MB Infinity Cache so that
+reads come from HBM. Prints one JSON line.
+
+Also measured: each kernel's average duration (HIP events around a graph of
+back-to-back launches of that kernel alone, on the stream it runs on), the
+attention roofline fraction, the budget-256 workload (batch 8, 256-node
+best-first trees, prefixes U[1024, 4096]) as `budget256`, and the fp64 CPU
+oracle on a bounded sample as `cpu_baseline`.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="c1_chain16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-budget256", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of graph replay")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run only this many eager steps of each kernel (for rocprofv3) and exit")
+    return ap.parse_args()
+
+
+class DeviceSet:
+    """One copy of a workload's inputs and outputs in device memory."""
+
+    def __init__(self, wl, src=None):
+        dev = "cuda"
+        if src is None:
+            self.t = {k: getattr(wl, k).to(dev) for k in
+                      ("q", "k_pages", "v_pages", "block_table", "prefix_len", "k_tree", "v_tree", "parent")}
+            self.t["draft"] = wl.draft.to(dev) if wl.draft is not None else None
+            self.t["logits"] = wl.logits.to(dev) if wl.logits is not None else None
+            self.t["target_ids"] = wl.target_ids.to(dev) if wl.target_ids is not None else None
+        else:
+            self.t = {k: (None if v is None else v.clone()) for k, v in src.t.items()}
+        B, N = wl.B, wl.N
+        self.anc = torch.empty((B, N, 4), dtype=torch.uint64, device=dev)
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.bad = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.t["q"])
+        self.nxt = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def nbytes(self):
+        return sum(v.numel() * v.element_size() for v in self.t.values() if v is not None)
+
+
+def attention_work(wl, depth: np.ndarray):
+    """Algorithmic bytes and flops of one attention call: prefix K+V read once
+    per KV head, plus Q, tree K/V, output, ancestor bitset, block table; flops
+    count only the (query, key) pairs the mask keeps."""
+    elt = torch.finfo(wl.dtype).bits // 8
+    L = wl.prefix_len.numpy().astype(np.int64)
+    kv = int(L.sum()) * wl.Hkv * wl.D * 2 * elt
+    q = wl.B * wl.N * wl.Hq * wl.D * elt
+    tree_kv = 2 * wl.B * wl.N * wl.Hkv * wl.D * elt
+    out = q
+    anc = wl.B * wl.N * 32
+    table = int(((L + 15) // 16).sum()) * 4 + wl.B * 4
+    nbytes = kv + q + tree_kv + out + anc + table
+    pairs = int((L[:, None] + depth.astype(np.int64)).sum())
+    flops = 4 * wl.D * wl.Hq * pairs
+    return nbytes, flops
+
+
+def time_graph(fn_list, reps, stream):
+    """Capture fn_list (callables) back to back in one graph, replay `reps`
+    times between HIP events on `stream`; returns ms per callable."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fn_list:
+            f()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(fn_list))
+
+
+def make_steps(jf, wl, sets, with_accept=True):
+    def mask(s):
+        return lambda: jf.build_ancestor_mask(s.t["parent"], anc=s.anc, depth=s.depth, bad_tree=s.bad)
+
+    def attn(s):
+        return lambda: jf.tree_attention(s.t["q"], s.t["k_pages"], s.t["v_pages"], s.t["block_table"],
+                                         s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], s.anc,
+                                         sm_scale=wl.sm_scale, max_prefix_len=wl.max_prefix_len, out=s.out)
+
+    def accept(s):
+        return lambda: jf.tree_accept(s.t["parent"], s.anc, s.t["draft"], logits=s.t["logits"],
+                                      target_ids=s.t["target_ids"] if s.t["logits"] is None else None,
+                                      next_tokens=s.nxt, accept_len=s.alen, accepted_nodes=s.nodes,
+                                      bonus_token=s.bonus)
+
+    def step(s):
+        fs = [mask(s), attn(s)] + ([accept(s)] if with_accept else [])
+
+        def run():
+            for f in fs:
+                f()
+        return run
+
+    return ([mask(s) for s in sets], [attn(s) for s in sets], [accept(s) for s in sets],
+            [step(s) for s in sets])
+
+
+def rotation_sets(wl, base, budget_bytes=2 * MALL_BYTES, cap=64):
+    n = max(1, min(cap, math.ceil(budget_bytes / max(1, base.nbytes()))))
+    return [base] + [DeviceSet(wl, src=base) for _ in range(n - 1)]
+
+
+def cpu_baseline(wl, seconds):
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.build_ancestor_mask(wl.parent)
+        oracle.tree_attention(wl.q, wl.k_pages, wl.v_pages, wl.block_table, wl.prefix_len, wl.k_tree, wl.v_tree,
+                              wl.parent, wl.sm_scale)
+        nxt = oracle.target_choice(wl.logits)
+        oracle.tree_accept(wl.parent, wl.draft, nxt)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": wl.B * wl.N * steps / el, "unit": "tree-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full steps (mask + fp64 attention with dense mask + argmax over "
+                      f"{wl.B}x{wl.N}x{wl.vocab} logits + walk) of the same workload, {el:.1f} s, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if "RANK" in os.environ and int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only; launched with WORLD_SIZE > 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    from tree_causal_attention_jf_amd import binding as jf
+    from tree_causal_attention_jf_amd import workloads as W
+
+    log(f"[bench] building workload {args.config}")
+    wl = W.make_workload(args.config, 0)
+    base = DeviceSet(wl)
+    sets = rotation_sets(wl, base)
+    log(f"[bench] {len(sets)} input sets x {base.nbytes() / 1e6:.1f} MB")
+    stream = torch.cuda.Stream()
+    masks, attns, accepts, steps = make_steps(jf, wl, sets)
+
+    with torch.cuda.stream(stream):
+        for i in range(max(1, args.warmup)):
+            steps[i % len(sets)]()
+    torch.cuda.synchronize()
+
+    if args.profile_steps:
+        with torch.cuda.stream(stream):
+            for i in range(args.profile_steps):
+                steps[i % len(sets)]()
+        torch.cuda.synchronize()
+        log("[bench] profile run done")
+        return
+
+    depth = base.depth.cpu().numpy()
+    nbytes, flops = attention_work(wl, depth)
+
+    # ---- timed region: exactly K steps
+    if args.eager:
+        run = lambda i: steps[i % len(sets)]()
+    else:
+        graphs = []
+        for s_fn in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                s_fn()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(len(graphs)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % len(graphs)].replay()
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    value = wl.B * wl.N / (ms_step * 1e-3)
+    log(f"[bench] {K} steps: {ms_step * 1e3:.2f} us/step, {value / 1e6:.3f} M tree-tokens/s")
+
+    # ---- per-kernel durations (graph of back-to-back launches, HIP events on the launch stream)
+    reps = max(4, 2000 // len(sets))
+    t_mask = time_graph(masks, reps, stream)
+    t_attn = time_graph(attns, reps, stream)
+    t_acc = time_graph(accepts, reps, stream)
+    log(f"[bench] per launch: mask {t_mask * 1e3:.2f} us, attention {t_attn * 1e3:.2f} us, "
+        f"accept {t_acc * 1e3:.2f} us")
+    achieved = nbytes / (t_attn * 1e-3) / 1e9
+    rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+          "kernel": "tree_attn_bf16_kernel", "algorithmic_bytes": nbytes, "flops": flops,
+          "avg_launch_us": round(t_attn * 1e3, 3)}
+    logit_bytes = wl.logits.numel() * wl.logits.element_size() if wl.logits is not None else 0
+    result = {
+        "metric": "tree-attention tree-tokens/s + % HBM/MFMA roofline at budget 16 and 256",
+        "value": round(value, 1),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: Qwen3-8B attention layer, batch {wl.B}, {wl.N}-node chain, "
+                               f"prefix {wl.max_prefix_len} in shuffled 16-token pages, {wl.Hq}q/{wl.Hkv}kv, "
+                               f"d={wl.D}; step = mask + attention + accept over {wl.vocab}-way bf16 logits",
+                   "graph_replay": not args.eager, "input_sets": len(sets)},
+        "roofline": rl,
+        "kernels_us": {"build_ancestor_mask": round(t_mask * 1e3, 3), "tree_attention": round(t_attn * 1e3, 3),
+                       "tree_accept": round(t_acc * 1e3, 3),
+                       "accept_GBps": round(logit_bytes / (t_acc * 1e-3) / 1e9, 1) if logit_bytes else None},
+    }
+
+    # ---- budget 256 (attention only): batch 8, best-first trees, ragged prefixes
+    if not args.no_budget256:
+        del graphs
+        log("[bench] building workload c2_bf256_b8")
+        wl2 = W.make_workload("c2_bf256_b8", 0, with_accept=False)
+        b2 = DeviceSet(wl2)
+        sets2 = rotation_sets(wl2, b2, cap=8)
+        m2, a2, _, _ = make_steps(jf, wl2, sets2, with_accept=False)
+        with torch.cuda.stream(stream):
+            for f in m2:
+                f()
+            for f in a2:
+                f()
+        torch.cuda.synchronize()
+        nb2, fl2 = attention_work(wl2, b2.depth.cpu().numpy())
+        t2 = time_graph(a2, max(4, 400 // len(sets2)), stream)
+        tf = fl2 / (t2 * 1e-3) / 1e12
+        result["budget256"] = {
+            "workload": "c2_bf256_b8: batch 8, 256-node best-first trees, prefix U[1024,4096], 32q/8kv, d=128",
+            "tree_tokens_per_s": round(wl2.B * wl2.N / (t2 * 1e-3), 1), "attention_us": round(t2 * 1e3, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "hbm_GBps": round(nb2 / (t2 * 1e-3) / 1e9, 1), "flops": fl2, "algorithmic_bytes": nb2},
+            "input_sets": len(sets2)}
+        log(f"[bench] budget256: {t2 * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

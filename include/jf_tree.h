@@ -1,0 +1,198 @@
+/*
+ * jf_tree.h -- C ABI of the MI355X (gfx950) tree-causal attention and greedy
+ * tree-acceptance library (libjf_tree.so).
+ *
+ * The operations come from "JetFlow: Breaking the Scaling Ceiling of
+ * Speculative Decoding with Parallel Tree Drafting" as summarised on the
+ * gist.science pages:
+ *   - section 2 (method), tree-causal attention mask: each draft-tree node
+ *     attends to the input prefix and to its own ancestors in the tree (and,
+ *     on our reading, itself), never to descendants or unrelated siblings;
+ *   - section 3 (contributions): the tree is verified in one target pass over
+ *     a paged KV cache;
+ *   - lay summary / qxai.app commentary: the target keeps the drafted tokens
+ *     up to the first disagreement.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *     Scratch memory comes from the caller's `workspace`.
+ *   - Every call is asynchronous on `stream` and never synchronises.
+ *   - A host-checkable argument error returns a non-zero jf_status before any
+ *     launch; nothing is written. Errors that only the device can see (an
+ *     invalid tree, an out-of-range page id or prefix length) are reported as
+ *     described for each call.
+ *   - Trees: N nodes numbered in creation order, 1 <= N <= 256,
+ *     parent[0] = -1 and 0 <= parent[i] < i for i > 0. Node 0 is the last
+ *     committed token; nodes 1..N-1 are drafts.
+ *   - Ancestor bitset `anc`: uint64 [B, N, 4]; node j is bit (j % 64) of word
+ *     (j / 64); row i has the bits of every node on the root-to-i path,
+ *     i itself included. Bits >= N are zero.
+ *   - Thread safety: the library keeps no mutable global state. Two calls in
+ *     flight at the same time must not share a workspace.
+ */
+#ifndef JF_TREE_H
+#define JF_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t jf_status;
+enum {
+    JF_OK = 0,
+    JF_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    JF_ERR_SHAPE = 2,        /* a size is out of range or inconsistent          */
+    JF_ERR_DTYPE = 3,        /* unknown dtype code                              */
+    JF_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. D not 64/128)   */
+    JF_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required         */
+    JF_ERR_LAUNCH = 6,       /* the HIP runtime refused a launch                */
+    JF_ERR_ALIGN = 7         /* a pointer is not 16-byte aligned                */
+};
+
+/* Element types of floating-point arrays. */
+enum { JF_F32 = 0, JF_BF16 = 1 };
+
+/* Longest tree the 256-bit ancestor bitset can describe. */
+#define JF_MAX_NODES 256
+#define JF_PAGE_SIZE 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* jf_status_string(jf_status s);
+
+/* Library version, e.g. "0.1.0" (static string). */
+const char* jf_version(void);
+
+/*
+ * jf_build_ancestor_mask -- the per-node ancestor bitset of a batch of trees
+ * (section 2, tree-causal attention mask).
+ *
+ *   parent    int32  [B, N]     parent of each node (see Trees above)
+ *   anc       uint64 [B, N, 4]  out: ancestor-or-self bitset
+ *   depth     int32  [B, N]     out, nullable: nodes on the root-to-node path
+ *                               (root = 1) = popcount of the row of anc
+ *   bad_tree  int32  [B]        out, nullable: 1 if that sequence's parent
+ *                               array breaks the tree rules, else 0
+ *
+ * For a flagged sequence, every parent entry that breaks the rules is read
+ * as -1 (a root), so anc/depth stay well defined but do not describe the
+ * intended tree. Host errors: JF_ERR_NULL (parent or anc NULL),
+ * JF_ERR_SHAPE (B < 0, N < 1 or N > 256). B = 0 is a no-op.
+ */
+jf_status jf_build_ancestor_mask(const int32_t* parent, int32_t B, int32_t N,
+                                 uint64_t* anc, int32_t* depth, int32_t* bad_tree,
+                                 hipStream_t stream);
+
+/* Shape of one tree-attention call. */
+typedef struct {
+    int32_t B;                 /* sequences                                        */
+    int32_t N;                 /* tree nodes per sequence, 1..256                  */
+    int32_t Hq;                /* query heads                                      */
+    int32_t Hkv;               /* KV heads; Hq % Hkv == 0; head h reads KV head h / (Hq/Hkv) */
+    int32_t D;                 /* head dimension: 64 or 128                        */
+    int32_t page_size;         /* tokens per KV page: must be 16                   */
+    int32_t num_pages;         /* pages in the pool: page ids are in [0, num_pages) */
+    int32_t max_pages_per_seq; /* columns of block_table                           */
+    int32_t dtype;             /* JF_BF16 or JF_F32, for q, pages, tree K/V and out */
+    float sm_scale;            /* score scale, usually 1/sqrt(D)                   */
+} jf_attn_shape;
+
+/*
+ * Bytes of workspace jf_tree_attention needs for this shape and prefix bound.
+ * Returns 0 for an invalid shape. The workspace must be zero-filled once
+ * before its first use (e.g. allocated with a zeroing allocator); every call
+ * leaves its counter region zero again, so it can be reused without
+ * clearing. The first 256 bytes of any size are part of the counter region.
+ */
+size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_prefix_len);
+
+/*
+ * jf_tree_attention -- tree-causal attention over a paged prefix
+ * (section 2 mask; section 3 paged verification).
+ *
+ *   s               host: shape (above)
+ *   max_prefix_len  host: upper bound on prefix_len[b]; sizes the grid.
+ *                   0 <= max_prefix_len <= max_pages_per_seq * page_size
+ *   q               [B, N, Hq, D]         queries of the tree nodes
+ *   k_pages,v_pages [num_pages, Hkv, page_size, D]  paged prefix cache
+ *   block_table     int32 [B, max_pages_per_seq]: prefix token t of sequence b
+ *                   is slot t % page_size of page block_table[b, t / page_size]
+ *   prefix_len      int32 [B]            prefix tokens of each sequence (may be 0)
+ *   k_tree,v_tree   [B, N, Hkv, D]       K/V of the tree nodes themselves
+ *   anc             uint64 [B, N, 4]     ancestor bitset (jf_build_ancestor_mask)
+ *   out             [B, N, Hq, D]        out, same dtype as q
+ *   lse             float [B, N, Hq]     out, nullable: natural-log log-sum-exp
+ *                                        of the scaled scores of each row
+ *   workspace       see jf_tree_attention_workspace_bytes
+ *
+ * Row (b, i, h) is softmax(sm_scale * q . k) over the L_b prefix keys and the
+ * tree keys j with bit j set in anc[b, i], times the matching values, with
+ * head h using KV head h / (Hq / Hkv). bf16 inputs use bf16 matrix cores
+ * with fp32 accumulation and an fp32 softmax; fp32 inputs are computed in
+ * fp32 throughout. Page slots at or beyond L_b and pages not in the table are
+ * never read into the result. If prefix_len[b] is outside
+ * [0, max_prefix_len] or a page id it needs is outside [0, num_pages), every
+ * output row of sequence b (and its lse) is set to NaN.
+ *
+ * Host errors: JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_DTYPE, JF_ERR_UNSUPPORTED
+ * (D not 64/128, page_size not 16), JF_ERR_ALIGN (q, pages, tree K/V, out or
+ * workspace not 16-byte aligned), JF_ERR_WORKSPACE, JF_ERR_LAUNCH.
+ */
+jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len,
+                            const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, const int32_t* prefix_len,
+                            const void* k_tree, const void* v_tree, const uint64_t* anc,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of workspace jf_tree_accept needs in logits mode (0 in ids mode is
+ * fine: pass target_logits = NULL). Same zero-fill rule as the attention
+ * workspace.
+ */
+size_t jf_tree_accept_workspace_bytes(int32_t B, int32_t N, int32_t vocab);
+
+/*
+ * jf_tree_accept -- greedy tree acceptance (lay summary: keep the drafted
+ * tokens up to the first disagreement; in a tree, the longest agreeing
+ * root-to-node path).
+ *
+ *   target_logits   [B, N, vocab] of logits_dtype, or NULL   (logits mode)
+ *   target_ids      int32 [B, N], or NULL                    (ids mode)
+ *                   exactly one of the two must be given
+ *   draft_tokens    int32 [B, N]   draft token of each node; column 0 unused
+ *   parent          int32 [B, N]
+ *   anc             uint64 [B, N, 4] (jf_build_ancestor_mask)
+ *   next_tokens     int32 [B, N]   out: target's token after each node =
+ *                   first index of the row's largest logit (NaN never wins,
+ *                   an all-NaN row gives 0), or a copy of target_ids
+ *   accept_len      int32 [B]      out: accepted draft tokens (path nodes - 1)
+ *   accepted_nodes  int32 [B, N]   out: root..end of the accepted path, then -1
+ *   bonus_token     int32 [B]      out: next_tokens at the end of the path
+ *
+ * Node u > 0 agrees when draft_tokens[u] == next_tokens[parent[u]]. The
+ * accepted path is the longest root-to-node path whose nodes all agree; ties
+ * go to the smallest end-node index. Results for a sequence whose parent
+ * array is not a valid tree are unspecified (memory-safe).
+ *
+ * Host errors: JF_ERR_NULL, JF_ERR_SHAPE (B < 0, N outside 1..256,
+ * vocab < 1, both or neither of logits/ids), JF_ERR_DTYPE, JF_ERR_WORKSPACE
+ * (logits mode), JF_ERR_LAUNCH.
+ */
+jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
+                         const void* target_logits, int32_t logits_dtype,
+                         const int32_t* target_ids,
+                         const int32_t* draft_tokens, const int32_t* parent, const uint64_t* anc,
+                         int32_t* next_tokens, int32_t* accept_len, int32_t* accepted_nodes,
+                         int32_t* bonus_token,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JF_TREE_H */

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host (those checks run
+before any HIP call, so they are safe without a device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "jf_tree.h")
+LIB = os.path.join(ROOT, "tree_causal_attention_jf_amd", "libjf_tree.so")
+
+JF_OK, JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_DTYPE, JF_ERR_UNSUPPORTED, JF_ERR_WORKSPACE, JF_ERR_LAUNCH, JF_ERR_ALIGN = range(8)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jf_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def binding():
+    if not os.path.exists(LIB):
+        pytest.fail("libjf_tree.so is not built (python -m tree_causal_attention_jf_amd.build)")
+    from tree_causal_attention_jf_amd import binding as B
+    return B
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
+               "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(binding):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (jf_\w+)$", out, flags=re.M))
+    for fn in _declared():
+        assert fn in exported, fn
+        assert hasattr(binding._lib, fn)
+    assert set(binding.EXPORTED) == set(_declared())
+
+
+def test_status_strings_and_version(binding):
+    for code in range(8):
+        assert binding.status_string(code)
+    assert binding.status_string(99) == "unknown status"
+    assert re.match(r"^\d+\.\d+\.\d+$", binding.version())
+
+
+def _shape(binding, **kw):
+    d = dict(B=1, N=16, Hq=32, Hkv=8, D=128, page_size=16, num_pages=128, max_pages_per_seq=128,
+             dtype=binding.JF_BF16, sm_scale=0.088)
+    d.update(kw)
+    return binding.AttnShape(**d)
+
+
+def _attn(binding, shape, max_prefix=2048, ptr=16, ws=None, ws_bytes=0, nullify=()):
+    args = {n: ctypes.c_void_p(ptr) for n in ("q", "kp", "vp", "bt", "pl", "kt", "vt", "anc", "out")}
+    for n in nullify:
+        args[n] = None
+    return binding._lib.jf_tree_attention(
+        ctypes.byref(shape) if shape is not None else None, max_prefix, args["q"], args["kp"], args["vp"],
+        args["bt"], args["pl"], args["kt"], args["vt"], args["anc"], args["out"], None, ws, ws_bytes, None)
+
+
+def test_attention_host_checks(binding):
+    L = binding._lib
+    assert L.jf_tree_attention(None, 0, *([None] * 10), None, 0, None) == JF_ERR_NULL
+    assert _attn(binding, _shape(binding, dtype=7)) == JF_ERR_DTYPE
+    assert _attn(binding, _shape(binding, N=0)) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, N=257)) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, Hq=30)) == JF_ERR_SHAPE          # Hq % Hkv != 0
+    assert _attn(binding, _shape(binding, B=-1)) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, D=96)) == JF_ERR_UNSUPPORTED
+    assert _attn(binding, _shape(binding, page_size=32)) == JF_ERR_UNSUPPORTED
+    assert _attn(binding, _shape(binding), max_prefix=2049) == JF_ERR_SHAPE  # beyond the table
+    assert _attn(binding, _shape(binding), max_prefix=-1) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, num_pages=0)) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, sm_scale=0.0)) == JF_ERR_SHAPE
+    assert _attn(binding, _shape(binding, sm_scale=float("inf"))) == JF_ERR_SHAPE
+    for n in ("q", "pl", "kt", "vt", "anc", "out", "kp", "vp", "bt"):
+        assert _attn(binding, _shape(binding), nullify=(n,)) == JF_ERR_NULL, n
+    # without a prefix the paged arguments may be NULL; the next check (alignment) fires instead
+    assert _attn(binding, _shape(binding), max_prefix=0, ptr=8, nullify=("kp", "vp", "bt")) == JF_ERR_ALIGN
+    assert _attn(binding, _shape(binding), ptr=8) == JF_ERR_ALIGN
+    # bf16 with many splits needs a workspace
+    need = binding.tree_attention_workspace_bytes(_shape(binding), 2048)
+    assert need > 0
+    assert _attn(binding, _shape(binding)) == JF_ERR_WORKSPACE
+    assert _attn(binding, _shape(binding), ws=ctypes.c_void_p(16), ws_bytes=need - 1) == JF_ERR_WORKSPACE
+    assert _attn(binding, _shape(binding), ws=ctypes.c_void_p(8), ws_bytes=need) == JF_ERR_ALIGN
+
+
+def test_workspace_queries(binding):
+    # fp32 never needs scratch; an invalid shape reports 0
+    assert binding.tree_attention_workspace_bytes(_shape(binding, dtype=binding.JF_F32), 2048) == 0
+    assert binding.tree_attention_workspace_bytes(_shape(binding, D=96), 2048) == 0
+    # a single split needs none either
+    assert binding.tree_attention_workspace_bytes(_shape(binding), 0) == 0
+    a = binding.tree_attention_workspace_bytes(_shape(binding, B=8, N=256, num_pages=2048, max_pages_per_seq=256), 4096)
+    b = binding.tree_attention_workspace_bytes(_shape(binding, B=8, N=256, num_pages=2048, max_pages_per_seq=256), 1024)
+    assert a >= b >= 0
+    assert binding.tree_accept_workspace_bytes(4, 256, 151936) > 4 * 256 * 4
+    assert binding.tree_accept_workspace_bytes(0, 0, 10) == 0
+
+
+def test_mask_and_accept_host_checks(binding):
+    L = binding._lib
+    p = ctypes.c_void_p(16)
+    assert L.jf_build_ancestor_mask(p, 1, 0, p, None, None, None) == JF_ERR_SHAPE
+    assert L.jf_build_ancestor_mask(p, 1, 257, p, None, None, None) == JF_ERR_SHAPE
+    assert L.jf_build_ancestor_mask(p, -1, 4, p, None, None, None) == JF_ERR_SHAPE
+    assert L.jf_build_ancestor_mask(None, 1, 4, p, None, None, None) == JF_ERR_NULL
+    assert L.jf_build_ancestor_mask(p, 1, 4, None, None, None, None) == JF_ERR_NULL
+    assert L.jf_build_ancestor_mask(p, 0, 4, p, None, None, None) == JF_OK   # empty batch: no launch
+
+    def acc(B=1, N=8, V=1000, logits=p, dt=1, ids=None, nul=(), ws=None, wsb=0):
+        a = {n: p for n in ("draft", "parent", "anc", "next", "alen", "nodes", "bonus")}
+        for n in nul:
+            a[n] = None
+        return L.jf_tree_accept(B, N, V, logits, dt, ids, a["draft"], a["parent"], a["anc"], a["next"],
+                                a["alen"], a["nodes"], a["bonus"], ws, wsb, None)
+
+    assert acc(N=0) == JF_ERR_SHAPE
+    assert acc(V=0) == JF_ERR_SHAPE
+    assert acc(logits=None) == JF_ERR_SHAPE            # neither logits nor ids
+    assert acc(ids=p) == JF_ERR_SHAPE                  # both
+    assert acc(dt=5) == JF_ERR_DTYPE
+    assert acc() == JF_ERR_WORKSPACE
+    need = binding.tree_accept_workspace_bytes(1, 8, 1000)
+    assert acc(ws=ctypes.c_void_p(8), wsb=need) == JF_ERR_ALIGN
+    for n in ("draft", "parent", "anc", "next", "alen", "nodes", "bonus"):
+        assert acc(nul=(n,)) == JF_ERR_NULL, n
+    assert acc(B=0, ws=ctypes.c_void_p(16), wsb=need) == JF_OK   # empty batch: no launch

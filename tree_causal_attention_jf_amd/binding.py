@@ -1,0 +1,252 @@
+"""ctypes binding over libjf_tree.so (include/jf_tree.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. torch supplies device memory (tensor.data_ptr()) and the current HIP
+stream. If the library is missing, importing this module raises: there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjf_tree.so")
+
+JF_F32, JF_BF16 = 0, 1
+MAX_NODES = 256
+PAGE_SIZE = 16
+
+EXPORTED = (
+    "jf_status_string",
+    "jf_version",
+    "jf_build_ancestor_mask",
+    "jf_tree_attention_workspace_bytes",
+    "jf_tree_attention",
+    "jf_tree_accept_workspace_bytes",
+    "jf_tree_accept",
+)
+
+
+class JfError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("N", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m tree_causal_attention_jf_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.jf_status_string.restype = ctypes.c_char_p
+    lib.jf_status_string.argtypes = [i32]
+    lib.jf_version.restype = ctypes.c_char_p
+    lib.jf_version.argtypes = []
+    lib.jf_build_ancestor_mask.restype = i32
+    lib.jf_build_ancestor_mask.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+    lib.jf_tree_attention_workspace_bytes.restype = sz
+    lib.jf_tree_attention_workspace_bytes.argtypes = [ctypes.POINTER(AttnShape), i32]
+    lib.jf_tree_attention.restype = i32
+    lib.jf_tree_attention.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
+    lib.jf_tree_accept_workspace_bytes.restype = sz
+    lib.jf_tree_accept_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.jf_tree_accept.restype = i32
+    lib.jf_tree_accept.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    return lib
+
+
+_lib = load_library()
+
+
+def status_string(status: int) -> str:
+    return _lib.jf_status_string(status).decode()
+
+
+def version() -> str:
+    return _lib.jf_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise JfError(fn, status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ------------------------------------------------------------------ workspaces
+
+class Workspace:
+    """Zero-initialised scratch buffers, one per (device, purpose). The
+    library leaves its counter region zero after every call, so a buffer is
+    cleared only when it is first allocated or grown. Not for calls that are
+    in flight concurrently on different streams."""
+
+    def __init__(self):
+        self._bufs = {}
+        self._lock = threading.Lock()
+
+    def get(self, device: torch.device, key: str, nbytes: int) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        with self._lock:
+            k = (str(device), key)
+            buf = self._bufs.get(k)
+            if buf is None or buf.numel() < nbytes:
+                buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+                self._bufs[k] = buf
+            return buf
+
+
+_default_ws = Workspace()
+
+
+# ------------------------------------------------------------------ entry points
+
+def build_ancestor_mask(parent: torch.Tensor, anc: Optional[torch.Tensor] = None,
+                        depth: Optional[torch.Tensor] = None, bad_tree: Optional[torch.Tensor] = None,
+                        with_depth: bool = True):
+    """parent int32 [B, N] -> (anc uint64 [B, N, 4], depth int32 [B, N], bad_tree int32 [B])."""
+    _need(parent, "parent", torch.int32)
+    B, N = parent.shape
+    dev = parent.device
+    if anc is None:
+        anc = torch.empty((B, N, 4), dtype=torch.uint64, device=dev)
+    if depth is None and with_depth:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if bad_tree is None:
+        bad_tree = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(anc, "anc", torch.uint64, (B, N, 4))
+    st = _lib.jf_build_ancestor_mask(_ptr(parent), B, N, _ptr(anc), _ptr(depth), _ptr(bad_tree), _stream(dev))
+    _check("jf_build_ancestor_mask", st)
+    return anc, depth, bad_tree
+
+
+def attn_shape(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor, sm_scale: Optional[float]):
+    B, N, Hq, D = q.shape
+    P, Hkv, page, Dk = k_pages.shape
+    dt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return AttnShape(B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, page_size=page, num_pages=P,
+                     max_pages_per_seq=block_table.shape[1], dtype=dt,
+                     sm_scale=float(1.0 / math.sqrt(D) if sm_scale is None else sm_scale))
+
+
+def tree_attention_workspace_bytes(shape: AttnShape, max_prefix_len: int) -> int:
+    return int(_lib.jf_tree_attention_workspace_bytes(ctypes.byref(shape), int(max_prefix_len)))
+
+
+def tree_attention(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc,
+                   sm_scale: Optional[float] = None, max_prefix_len: Optional[int] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Tree-causal attention (see include/jf_tree.h). max_prefix_len is a host
+    upper bound on prefix_len; when None it is read from the device (a sync)."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (k_tree, "k_tree"), (v_tree, "v_tree")):
+        _need(t, n, q.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(prefix_len, "prefix_len", torch.int32)
+    _need(anc, "anc", torch.uint64)
+    shape = attn_shape(q, k_pages, block_table, sm_scale)
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_len.max().item()) if prefix_len.numel() else 0
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    need = tree_attention_workspace_bytes(shape, max_prefix_len)
+    ws = workspace if workspace is not None else _default_ws.get(dev, "attn", need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib.jf_tree_attention(ctypes.byref(shape), int(max_prefix_len), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc),
+                                _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev))
+    _check("jf_tree_attention", st)
+    return (out, lse) if return_lse else out
+
+
+def tree_accept_workspace_bytes(B: int, N: int, vocab: int) -> int:
+    return int(_lib.jf_tree_accept_workspace_bytes(B, N, vocab))
+
+
+def tree_accept(parent, anc, draft, logits: Optional[torch.Tensor] = None,
+                target_ids: Optional[torch.Tensor] = None, next_tokens=None, accept_len=None,
+                accepted_nodes=None, bonus_token=None, workspace: Optional[torch.Tensor] = None):
+    """Greedy tree acceptance. Exactly one of logits [B, N, V] (bf16/fp32) or
+    target_ids int32 [B, N]. Returns (accept_len, accepted_nodes, bonus, next_tokens)."""
+    _need(parent, "parent", torch.int32)
+    _need(draft, "draft", torch.int32)
+    _need(anc, "anc", torch.uint64)
+    B, N = parent.shape
+    dev = parent.device
+    if (logits is None) == (target_ids is None):
+        raise ValueError("pass exactly one of logits / target_ids")
+    if logits is not None:
+        _need(logits, "logits")
+        vocab = logits.shape[-1]
+        ldt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}[logits.dtype]
+    else:
+        _need(target_ids, "target_ids", torch.int32)
+        vocab, ldt = 1, JF_F32
+    if next_tokens is None:
+        next_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = workspace
+    ws_bytes = 0
+    if logits is not None:
+        need = tree_accept_workspace_bytes(B, N, vocab)
+        if ws is None:
+            ws = _default_ws.get(dev, "accept", need)
+        ws_bytes = ws.numel() * ws.element_size()
+    st = _lib.jf_tree_accept(B, N, vocab, _ptr(logits), ldt, _ptr(target_ids), _ptr(draft), _ptr(parent),
+                             _ptr(anc), _ptr(next_tokens), _ptr(accept_len), _ptr(accepted_nodes),
+                             _ptr(bonus_token), _ptr(ws), ws_bytes, _stream(dev))
+    _check("jf_tree_accept", st)
+    return accept_len, accepted_nodes, bonus_token, next_tokens

@@ -1,0 +1,137 @@
+// C ABI of libjf_tree: argument checks, workspace sizing and launches.
+// Every check here runs on the host before any HIP call, so a rejected call
+// touches neither the device nor the caller's buffers.
+#include <math.h>
+
+#include "jf_common.h"
+
+namespace jf {
+hipError_t launch_ancestor_mask(const int32_t* parent, int B, int N, uint64_t* anc, int32_t* depth,
+                                int32_t* bad_tree, hipStream_t stream);
+hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
+                                 const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                                 const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
+                                 float* lse, void* workspace, hipStream_t stream);
+hipError_t launch_attention_f32(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
+                                const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                                const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
+                                float* lse, hipStream_t stream);
+size_t attention_bf16_workspace_bytes(const jf_attn_shape& s, int max_prefix);
+hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype, const int32_t* target_ids,
+                         const int32_t* draft, const int32_t* parent, const uint64_t* anc, int32_t* next_tokens,
+                         int32_t* accept_len, int32_t* accepted_nodes, int32_t* bonus, void* workspace,
+                         hipStream_t stream);
+size_t accept_workspace_bytes(int B, int N, int vocab);
+}  // namespace jf
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+jf_status check_attn_shape(const jf_attn_shape* s, int32_t max_prefix_len) {
+    if (!s) return JF_ERR_NULL;
+    if (s->dtype != JF_F32 && s->dtype != JF_BF16) return JF_ERR_DTYPE;
+    if (s->B < 0 || s->N < 1 || s->N > JF_MAX_NODES || s->Hq < 1 || s->Hkv < 1 || s->Hq % s->Hkv != 0)
+        return JF_ERR_SHAPE;
+    if (s->num_pages < 0 || s->max_pages_per_seq < 0) return JF_ERR_SHAPE;
+    if (s->D != 64 && s->D != 128) return JF_ERR_UNSUPPORTED;
+    if (s->page_size != JF_PAGE_SIZE) return JF_ERR_UNSUPPORTED;
+    if (max_prefix_len < 0 || (long)max_prefix_len > (long)s->max_pages_per_seq * JF_PAGE_SIZE) return JF_ERR_SHAPE;
+    if (max_prefix_len > 0 && s->num_pages < 1) return JF_ERR_SHAPE;
+    if (!(s->sm_scale > 0.f) || !isfinite(s->sm_scale)) return JF_ERR_SHAPE;
+    // index arithmetic inside the kernels: grid and row counts fit 32 bits
+    const long rows = (long)(s->Hq / s->Hkv) * s->N;
+    if ((long)s->B * s->Hkv * ((rows + 63) / 64) * ((max_prefix_len / 64) + 1) > 0x7fffffffL) return JF_ERR_SHAPE;
+    return JF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jf_status_string(jf_status s) {
+    switch (s) {
+        case JF_OK: return "ok";
+        case JF_ERR_NULL: return "a required pointer is NULL";
+        case JF_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case JF_ERR_DTYPE: return "unknown dtype code";
+        case JF_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128, page size 16)";
+        case JF_ERR_WORKSPACE: return "workspace missing or too small";
+        case JF_ERR_LAUNCH: return "kernel launch failed";
+        case JF_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+const char* jf_version(void) { return "0.1.0"; }
+
+jf_status jf_build_ancestor_mask(const int32_t* parent, int32_t B, int32_t N, uint64_t* anc, int32_t* depth,
+                                 int32_t* bad_tree, hipStream_t stream) {
+    if (B < 0 || N < 1 || N > JF_MAX_NODES) return JF_ERR_SHAPE;
+    if (!parent || !anc) return JF_ERR_NULL;
+    if (B == 0) return JF_OK;
+    return jf::launch_ancestor_mask(parent, B, N, anc, depth, bad_tree, stream) == hipSuccess ? JF_OK
+                                                                                              : JF_ERR_LAUNCH;
+}
+
+size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_prefix_len) {
+    if (check_attn_shape(s, max_prefix_len) != JF_OK) return 0;
+    if (s->dtype == JF_F32) return 0;
+    return jf::attention_bf16_workspace_bytes(*s, max_prefix_len);
+}
+
+jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                            const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const jf_status st = check_attn_shape(s, max_prefix_len);
+    if (st != JF_OK) return st;
+    if (!q || !prefix_len || !k_tree || !v_tree || !anc || !out) return JF_ERR_NULL;
+    if (max_prefix_len > 0 && (!k_pages || !v_pages || !block_table)) return JF_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_tree) || !aligned16(v_tree) ||
+        !aligned16(out))
+        return JF_ERR_ALIGN;
+    const size_t need = jf_tree_attention_workspace_bytes(s, max_prefix_len);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return JF_ERR_ALIGN;
+    }
+    if (s->B == 0) return JF_OK;
+    hipError_t e;
+    if (s->dtype == JF_BF16)
+        e = jf::launch_attention_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                      v_tree, anc, out, lse, workspace, stream);
+    else
+        e = jf::launch_attention_f32(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                     v_tree, anc, out, lse, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+size_t jf_tree_accept_workspace_bytes(int32_t B, int32_t N, int32_t vocab) {
+    if (B < 0 || N < 1 || N > JF_MAX_NODES || vocab < 1) return 0;
+    return jf::accept_workspace_bytes(B, N, vocab);
+}
+
+jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target_logits, int32_t logits_dtype,
+                         const int32_t* target_ids, const int32_t* draft_tokens, const int32_t* parent,
+                         const uint64_t* anc, int32_t* next_tokens, int32_t* accept_len, int32_t* accepted_nodes,
+                         int32_t* bonus_token, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || N < 1 || N > JF_MAX_NODES || vocab < 1) return JF_ERR_SHAPE;
+    if ((target_logits == nullptr) == (target_ids == nullptr)) return JF_ERR_SHAPE;
+    if (!draft_tokens || !parent || !anc || !next_tokens || !accept_len || !accepted_nodes || !bonus_token)
+        return JF_ERR_NULL;
+    if (target_logits) {
+        if (logits_dtype != JF_F32 && logits_dtype != JF_BF16) return JF_ERR_DTYPE;
+        const size_t need = jf::accept_workspace_bytes(B, N, vocab);
+        if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return JF_ERR_ALIGN;
+        if ((long)B * N * ((vocab + 4095) / 4096) > 0x7fffffffL) return JF_ERR_SHAPE;
+    }
+    if (B == 0) return JF_OK;
+    const hipError_t e = jf::launch_accept(B, N, vocab, target_logits, logits_dtype, target_ids, draft_tokens,
+                                           parent, anc, next_tokens, accept_len, accepted_nodes, bonus_token,
+                                           workspace, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+}  // extern "C"
