@@ -7,10 +7,11 @@
 //
 // Logits mode runs as ONE launch. The vocabulary of each row is cut into C
 // chunks; workgroup (row, chunk) streams its chunk with 16-byte loads and
-// keeps the best (value, index) pair. The last chunk of a row to finish
-// (agent-scope counter) merges the C pairs and writes next_tokens[row]; the
-// last row of a sequence to finish then runs the walk for that sequence. All
-// counters return to zero, so the workspace never needs clearing again.
+// publishes its winner as one order-preserving 64-bit key (value, then the
+// smaller index). The last of a sequence's N * C workgroups to finish (one
+// agent-scope counter per sequence) merges the keys with LDS atomic max, writes
+// next_tokens, and runs the walk from LDS. The counters return to zero, so the
+// workspace never needs clearing again.
 #include "jf_common.h"
 
 namespace jf {
@@ -37,6 +38,19 @@ __device__ __forceinline__ void offer(Best& b, float v, int i) {
 
 __device__ __forceinline__ Best merge(Best a, Best b) { return better(b.v, b.i, a) ? b : a; }
 
+// (value, index) -> 64-bit key whose unsigned order is `better`'s order:
+// high word = the float's bits mapped to an order-preserving unsigned (with -0
+// read as +0), low word = ~index. An empty winner (no non-NaN value) is 0,
+// below every real key.
+__device__ __forceinline__ uint64_t best_key(Best b) {
+    if (b.i == kNoIndex) return 0ull;
+    uint32_t u = __float_as_uint(b.v == 0.f ? 0.f : b.v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)b.i);
+}
+
+__device__ __forceinline__ int key_index(uint64_t k) { return k == 0ull ? 0 : (int)(~(uint32_t)k); }
+
 __device__ Best block_best(Best b, Best* scratch) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -55,13 +69,14 @@ __device__ Best block_best(Best b, Best* scratch) {
     return r;
 }
 
-// One sequence's walk, run by a whole 256-thread workgroup (N <= 256).
-//   mism bit u: u > 0 and draft[u] != next[parent[u]]
+// One sequence's walk, run by a whole 256-thread workgroup (N <= 256); thread
+// u holds node u's parent, draft token and ancestor words; nxt[] is the
+// target's token after each node of the sequence (LDS or global).
+//   mism bit u: u > 0 and draft[u] != nxt[parent[u]]
 //   node v agrees along its path iff (anc[v] & mism) == 0
 //   end node = the agreeing node with most path nodes, smallest index on ties
-__device__ void walk_sequence(int b, int N, const int32_t* __restrict__ draft,
-                              const int32_t* __restrict__ parent, const uint64_t* __restrict__ anc,
-                              const int32_t* __restrict__ next, int32_t* __restrict__ accept_len,
+__device__ void walk_sequence(int b, int N, int p_u, int d_u, const uint64_t a_u[kAncWords],
+                              const int32_t* nxt, int32_t* __restrict__ accept_len,
                               int32_t* __restrict__ accepted_nodes, int32_t* __restrict__ bonus) {
     __shared__ uint64_t mism[kAncWords];
     __shared__ uint64_t end_set[kAncWords];
@@ -72,9 +87,8 @@ __device__ void walk_sequence(int b, int N, const int32_t* __restrict__ draft,
 
     bool bad = false;
     if (u > 0 && u < N) {
-        int p = parent[base + u];
-        p = (p < 0) ? 0 : (p >= N ? N - 1 : p);     // memory safety on broken trees
-        bad = draft[base + u] != next[base + p];
+        const int p = (p_u < 0) ? 0 : (p_u >= N ? N - 1 : p_u);   // memory safety on broken trees
+        bad = d_u != nxt[p];
     }
     const uint64_t ballot = __ballot(bad);
     if (lane == 0) mism[w] = ballot;
@@ -82,15 +96,13 @@ __device__ void walk_sequence(int b, int N, const int32_t* __restrict__ draft,
 
     // key = (path nodes << 16) | (0xffff - node) for agreeing nodes, else 0
     unsigned key = 0;
-    uint64_t mine[kAncWords] = {0, 0, 0, 0};
     if (u < N) {
         bool ok = true;
         int cnt = 0;
         #pragma unroll
         for (int k = 0; k < kAncWords; ++k) {
-            mine[k] = anc[(base + u) * kAncWords + k];
-            ok = ok && ((mine[k] & mism[k]) == 0);
-            cnt += __popcll(mine[k]);
+            ok = ok && ((a_u[k] & mism[k]) == 0);
+            cnt += __popcll(a_u[k]);
         }
         if (ok && cnt > 0) key = ((unsigned)cnt << 16) | (0xffffu - (unsigned)u);
     }
@@ -113,7 +125,7 @@ __device__ void walk_sequence(int b, int N, const int32_t* __restrict__ draft,
     if (nodes > N) nodes = N;
     if (u == v_end) {
         #pragma unroll
-        for (int k = 0; k < kAncWords; ++k) end_set[k] = mine[k];
+        for (int k = 0; k < kAncWords; ++k) end_set[k] = a_u[k];
     }
     __syncthreads();
     if (u < N) {
@@ -129,8 +141,27 @@ __device__ void walk_sequence(int b, int N, const int32_t* __restrict__ draft,
     }
     if (u == 0) {
         accept_len[b] = nodes - 1;
-        bonus[b] = next[base + v_end];
+        bonus[b] = nxt[v_end];
     }
+}
+
+struct NodeIn {
+    int p, d;
+    uint64_t a[kAncWords];
+};
+
+__device__ __forceinline__ NodeIn load_node(int b, int N, const int32_t* __restrict__ parent,
+                                            const int32_t* __restrict__ draft, const uint64_t* __restrict__ anc) {
+    NodeIn n{-1, 0, {0, 0, 0, 0}};
+    const int u = threadIdx.x;
+    if (u < N) {
+        const size_t r = (size_t)b * N + u;
+        n.p = parent[r];
+        n.d = draft[r];
+        #pragma unroll
+        for (int k = 0; k < kAncWords; ++k) n.a[k] = anc[r * kAncWords + k];
+    }
+    return n;
 }
 
 // ids mode: next_tokens = target_ids, then the walk. One workgroup per sequence.
@@ -139,8 +170,9 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_ids_kernel(
     const int32_t* __restrict__ parent, const uint64_t* __restrict__ anc, int32_t* __restrict__ next_tokens,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accepted_nodes, int32_t* __restrict__ bonus) {
     const int b = blockIdx.x;
+    const NodeIn nd = load_node(b, N, parent, draft, anc);
     if (threadIdx.x < N) next_tokens[(size_t)b * N + threadIdx.x] = target_ids[(size_t)b * N + threadIdx.x];
-    walk_sequence(b, N, draft, parent, anc, target_ids, accept_len, accepted_nodes, bonus);
+    walk_sequence(b, N, nd.p, nd.d, nd.a, target_ids + (size_t)b * N, accept_len, accepted_nodes, bonus);
 }
 
 template <typename T>
@@ -185,7 +217,19 @@ template <>
 __device__ __forceinline__ void scan_chunk<float>(const float* __restrict__ row, int lo, int hi, Best& b) {
     const int nvec = (hi - lo) >> 2;
     const f32x4* vp = reinterpret_cast<const f32x4*>(row + lo);
+    constexpr int U = 4;
     int k = threadIdx.x;
+    for (; k + (U - 1) * kAcceptThreads < nvec; k += U * kAcceptThreads) {
+        f32x4 r[U];
+        #pragma unroll
+        for (int j = 0; j < U; ++j) r[j] = __builtin_nontemporal_load(vp + k + j * kAcceptThreads);
+        #pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int i0 = lo + ((k + j * kAcceptThreads) << 2);
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) offer(b, r[j][e], i0 + e);
+        }
+    }
     for (; k < nvec; k += kAcceptThreads) {
         const f32x4 r = __builtin_nontemporal_load(vp + k);
         const int i0 = lo + (k << 2);
@@ -215,9 +259,8 @@ struct AcceptArgs {
     int32_t* accept_len;
     int32_t* accepted_nodes;
     int32_t* bonus;
-    int* row_count;     // [B*N]   (workspace, zero between calls)
-    int* seq_count;     // [B]     (workspace, zero between calls)
-    Best* partial;      // [B*N*C] (workspace)
+    int* seq_count;     // [B]       (workspace, zero between calls)
+    uint64_t* partial;  // [B*N*C]   chunk winners as keys (workspace)
     int N, vocab, chunks, chunk_len;
     int aligned;        // rows start on 16-byte boundaries and chunk_len keeps them there
 };
@@ -225,6 +268,8 @@ struct AcceptArgs {
 template <typename T>
 __global__ __launch_bounds__(kAcceptThreads) void accept_logits_kernel(AcceptArgs a) {
     __shared__ Best scratch[kAcceptThreads / kWave];
+    __shared__ unsigned long long s_key[JF_MAX_NODES];
+    __shared__ int32_t s_next[JF_MAX_NODES];
     __shared__ int last;
     const int blk = blockIdx.x;
     const int row = blk / a.chunks, c = blk - row * a.chunks;
@@ -238,47 +283,53 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_logits_kernel(AcceptArg
     else scan_scalar<T>(rp, lo, hi, best);
     best = block_best(best, scratch);
 
-    if (a.chunks > 1) {
-        if (threadIdx.x == 0) a.partial[blk] = best;
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const int old = arrive(&a.row_count[row]);
-            last = (old == a.chunks - 1);
-            if (last) reset_counter(&a.row_count[row]);
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-        // merge the row's chunk winners (order-independent: `better` is a strict total order)
-        Best m{-__builtin_inff(), kNoIndex};
-        for (int k = threadIdx.x; k < a.chunks; k += kAcceptThreads) {
-            const Best p = a.partial[(size_t)row * a.chunks + k];
-            if (p.i != kNoIndex) m = merge(m, p);
-        }
-        best = block_best(m, scratch);
-    }
-    if (threadIdx.x == 0) a.next_tokens[row] = (best.i == kNoIndex) ? 0 : best.i;
-
-    // sequence completion: the last finished row of sequence b runs the walk
-    __threadfence();
-    __syncthreads();
+    // publish the chunk winner; the sequence's last workgroup to finish goes on
+    const int per_seq = a.N * a.chunks;
     if (threadIdx.x == 0) {
+        __hip_atomic_store(&a.partial[blk], best_key(best), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_own_stores();
         const int old = arrive(&a.seq_count[b]);
-        last = (old == a.N - 1);
+        last = (old == per_seq - 1);
         if (last) reset_counter(&a.seq_count[b]);
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();
-    walk_sequence(b, a.N, a.draft, a.parent, a.anc, a.next_tokens, a.accept_len, a.accepted_nodes, a.bonus);
+
+    // every load of the final phase at once: this thread's node and up to 4
+    // chunk keys per pass (one pass covers N * C <= 1024)
+    const NodeIn nd = load_node(b, a.N, a.parent, a.draft, a.anc);
+    const uint64_t* pk = a.partial + (size_t)b * per_seq;
+    const int u = threadIdx.x;
+    if (u < a.N) s_key[u] = 0ull;
+    for (int k0 = 0; k0 < per_seq; k0 += 4 * kAcceptThreads) {
+        uint64_t kv[4];
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + u + j * kAcceptThreads;
+            kv[j] = (k < per_seq) ? __hip_atomic_load(pk + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        }
+        __syncthreads();                    // s_key initialised (first pass) / previous pass merged
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + u + j * kAcceptThreads;
+            if (k < per_seq) atomicMax(&s_key[k / a.chunks], (unsigned long long)kv[j]);
+        }
+    }
+    __syncthreads();
+    if (u < a.N) {
+        const int nx = key_index(s_key[u]);
+        s_next[u] = nx;
+        a.next_tokens[(size_t)b * a.N + u] = nx;
+    }
+    __syncthreads();
+    walk_sequence(b, a.N, nd.p, nd.d, nd.a, s_next, a.accept_len, a.accepted_nodes, a.bonus);
 }
 
 // ---------------------------------------------------------------- host side
 
 struct AcceptPlan {
     int chunks, chunk_len;
-    size_t off_row, off_seq, off_part, bytes;
+    size_t off_seq, off_part, bytes;
 };
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -286,8 +337,8 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 AcceptPlan plan_accept(int B, int N, int vocab) {
     AcceptPlan p{};
     const long rows = (long)B * N;
-    const int min_chunk = 4096;                        // >= 16 values per thread
-    int chunks = (int)((2048 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~2048 workgroups
+    const int min_chunk = 8192;                        // >= 32 values (4 loads) per thread
+    int chunks = (int)((1024 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~1024 workgroups
     const int max_chunks = (vocab + min_chunk - 1) / min_chunk;
     chunks = chunks < 1 ? 1 : chunks;
     chunks = chunks > max_chunks ? max_chunks : chunks;
@@ -297,10 +348,9 @@ AcceptPlan plan_accept(int B, int N, int vocab) {
     chunks = (vocab + len - 1) / len;
     p.chunks = chunks;
     p.chunk_len = len;
-    p.off_row = 0;
-    p.off_seq = align_up((size_t)rows * 4, 256);
-    p.off_part = p.off_seq + align_up((size_t)B * 4, 256);
-    p.bytes = p.off_part + align_up((size_t)rows * chunks * sizeof(Best), 256);
+    p.off_seq = 0;
+    p.off_part = align_up((size_t)B * 4, 256);
+    p.bytes = p.off_part + align_up((size_t)rows * chunks * 8, 256);
     return p;
 }
 
@@ -325,9 +375,8 @@ hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype,
     a.accept_len = accept_len;
     a.accepted_nodes = accepted_nodes;
     a.bonus = bonus;
-    a.row_count = reinterpret_cast<int*>(ws + p.off_row);
     a.seq_count = reinterpret_cast<int*>(ws + p.off_seq);
-    a.partial = reinterpret_cast<Best*>(ws + p.off_part);
+    a.partial = reinterpret_cast<uint64_t*>(ws + p.off_part);
     a.N = N;
     a.vocab = vocab;
     a.chunks = p.chunks;

@@ -10,36 +10,45 @@
 // Work decomposition
 //   * GQA packing: the G*N query rows that share one KV head form one matrix
 //     (row r = node * G + g), so every K/V tile is staged once per KV head.
-//   * A workgroup owns RB = 32 * NW consecutive rows (NW waves, 32 rows per
-//     wave) of one (sequence, KV head) and a contiguous run of prefix pages
-//     (a "split"). The split that owns the last prefix page also runs the tree
-//     block. Splits of one row block are merged in the same launch by the last
-//     one to finish (agent-scope counter), in split order.
+//   * A workgroup owns RB = 32 * RW consecutive rows of one (sequence, KV
+//     head) and a contiguous run of prefix pages (a "split"). The split that
+//     owns the last prefix page also runs the tree block.
+//   * Its RW * KW waves form RW row groups (32 rows each) times KW key groups:
+//     key group k multiplies tiles k, k + KW, k + 2 KW, ... of the split, so
+//     small row counts still keep many tiles in flight per workgroup. Key
+//     groups are merged in LDS at the end.
+//   * Splits of one row block are merged in the same launch by the last one
+//     to finish (agent-scope counter), in split order, with every thread's
+//     loads in flight at once.
 //   * Workgroup ids are remapped so that the row blocks and splits of one KV
 //     head land on one XCD and share its L2.
 //
-// Per 64-key tile, per wave (32 query rows):
-//   S^T[key, row] = K_tile Q^T         8 (D=128) v_mfma_f32_32x32x16_bf16 per 32 keys
-//   online softmax in fp32 per row (exp2 with the scale folded into log2 e)
-//   O^T[d, row]  += V_tile^T P^T       P is rounded to bf16 for the product
-// With S^T in the matrix-core output layout each lane owns one query row and
-// 16 keys per 32-key block, so the 256-bit ancestor bitset of that row's node
-// sits in the lane's registers and masking is a per-register bit test.
+// Data movement: 64-key tiles of K and V go from HBM straight into a 4-tile
+// LDS ring with global_load_lds_dwordx4 (16 bytes per lane, no staging
+// registers), rounds of KW tiles ahead of the ones being multiplied; each wave
+// counts its own transfers with vmcnt and a barrier publishes a round to all
+// waves. Rows are stored as they are in the cache (key-major), 16-byte chunks
+// XOR-swizzled per key so that the matrix-operand reads are bank-conflict free.
 //
-// LDS layout (16-byte chunks, XOR-swizzled so the matrix-operand reads are
-// bank-conflict free):
-//   K  [64 keys][D]   chunk c of key k stored at chunk c ^ (k & 7)
-//   V^T[D][64 keys]   keys permuted inside each 16-key group so one 16-byte
-//                     read gives a lane the 8 keys its P^T registers hold;
-//                     chunk c of row d stored at c ^ ((d ^ (d >> 3)) & 7)
-// Global -> register -> LDS staging is double buffered: the loads of tile t+1
-// are in flight while tile t is multiplied.
+// Per tile, per wave (32 query rows):
+//   S^T[key, row] = K_tile Q^T     (A = K rows via ds_read_b128, B = Q in registers)
+//   online softmax in fp32 per row (exp2 with the scale folded into log2 e;
+//   the running max is only moved when it grows by more than 2^8, so the
+//   output accumulators are rarely rescaled)
+//   O^T[d, row]  += V^T P^T        (A = V^T via ds_read_b64_tr_b16, which
+//                                   transposes 4 keys x 16 d per 16 lanes;
+//                                   B = P^T in registers, rounded to bf16)
+// In the matrix-core output layout each lane owns one query row and 16 keys
+// per 32-key block, so the 256-bit ancestor bitset of that row's node sits in
+// the lane's registers and masking is a per-register bit test.
 #include "jf_common.h"
 
 namespace jf {
 
 constexpr int kKeyTile = 64;
+constexpr int kRing = 4;                 // LDS tile buffers
 constexpr int kMaxPagesPerSplit = 1024;
+constexpr int kMaxSplits = 64;
 
 struct AttnArgs {
     const uint16_t* q;
@@ -55,6 +64,7 @@ struct AttnArgs {
     int* counters;     // [items]                       zero between calls
     float* part_ml;    // [items][splits][RB][2]        (m in log2 units, l)
     float* part_o;     // [items][splits][RB][D]        unnormalised
+    uint32_t part_ml_bytes, part_o_bytes;
     int B, N, Hq, Hkv, G, num_pages, max_pages, max_prefix;
     int rows;          // G * N
     int nrb;           // row blocks per (sequence, KV head)
@@ -63,130 +73,255 @@ struct AttnArgs {
     float scale_log2;  // sm_scale * log2(e)
 };
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-template <int D, int NW>
-struct Tile {
-    static constexpr int T = NW * kWave;          // threads
-    static constexpr int CPR = D / 8;             // 16-byte chunks per key row
-    static constexpr int KCH = kKeyTile * CPR / T;                   // K chunks per thread
-    static constexpr int VUNITS = (kKeyTile / 4) * CPR;              // 4-key x 8-d units
-    static constexpr int VU = (VUNITS + T - 1) / T;                  // V units per thread
-    static constexpr int K_BYTES = kKeyTile * D * 2;
-    static constexpr int V_BYTES = D * kKeyTile * 2;
-    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-    static_assert(kKeyTile * CPR % T == 0, "K tile must split evenly over threads");
+template <int D>
+struct Geo {
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int CPR = D / 8;                       // 16-byte chunks per key row
+    static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;    // key rows per 1 KB transfer
+    static constexpr int TILE_BYTES = kKeyTile * ROW_BYTES; // one of K or V
+    static constexpr int KB_PER_TILE = TILE_BYTES / 1024;
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES;        // K then V
+    static constexpr int XFER_PER_TILE = 2 * KB_PER_TILE;   // 1 KB transfers per tile
 };
 
-// Byte offset of 16-byte chunk c of key k in the K tile.
+// Chunk swizzles for gfx950's 64-bank LDS, where one access cycle serves 256
+// bytes (16 lanes of a 16-byte read):
+//  K is read 16 keys at a time at one logical chunk (QK operand): the 16 keys
+//    must land on 16 distinct 16-byte bank groups;
+//  V is read 4 consecutive keys x 2 adjacent chunks per 16 lanes, two such
+//    groups (chunk pairs 0-1 and 2-3 of a 4-chunk block) per 32 lanes
+//    (transposing PV operand): the 4 keys x 4 chunks must be distinct.
+// Rows are 256 bytes (D = 128, one row per bank window) or 128 bytes (D = 64,
+// two rows per window, so the low key bit picks the half).
 template <int D>
-__device__ __forceinline__ int k_off(int k, int c) {
-    return k * (D * 2) + ((c ^ (k & 7)) << 4);
+__device__ __forceinline__ int swz_k(int key) {
+    return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int key) {
+    return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
 }
 
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Byte offset of 16-byte chunk c of row d in the V^T tile (64 keys = 128 bytes per row).
-__device__ __forceinline__ int vt_off(int d, int c) { return d * (kKeyTile * 2) + ((c ^ vt_swz(d)) << 4); }
+// One 16-byte-per-lane transfer from global memory into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
 
-template <int D, int NW>
-struct Stage {
-    u32x4 k[Tile<D, NW>::KCH];
-    u32x4 v[Tile<D, NW>::VU][4];
-};
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-// Element offset (within k_pages/v_pages or k_tree/v_tree) of key `key` of a
-// tile, or -1 when that key is outside the tile's valid range.
 struct TileSrc {
     bool tree;
     int t0;        // prefix: first token of the tile; tree: first node
     int limit;     // prefix: one past the last valid token; tree: N
 };
 
+// Issue this wave's share (transfers first .. first + CNT - 1 of a round) of
+// the transfers of one round of KW tiles into LDS starting at `buf`. Tile j of
+// the round goes to buf + j * BUF_BYTES; K transfers first, then V. Keys
+// beyond a tile's valid range are fetched from the tile's first key instead
+// (always valid); the softmax masks them, and they are finite, so a zero
+// weight times them stays zero. A round slot past the last tile re-fetches the
+// last tile (the slot is never multiplied), which keeps every wave's transfer
+// count per round fixed for the vmcnt bookkeeping. All addresses (and the page
+// ids they need from LDS) are formed before the first transfer is issued.
+template <int D, int CNT, typename SrcFn>
+__device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* vp, const uint16_t* kt,
+                                            const uint16_t* vt, int N, int Hkv, SrcFn tile_src, int round_first_tile,
+                                            int n_tiles,
+                                            int b, int kvh, int p_begin, const int* s_pages, uint32_t buf,
+                                            int first, int lane) {
+    using Gm = Geo<D>;
+    const int rsub = lane / Gm::CPR, pc = lane % Gm::CPR;
+    constexpr int BATCH = CNT < 4 ? CNT : 4;
+    static_assert(CNT % BATCH == 0, "transfer count must be a multiple of the batch");
+    #pragma unroll
+    for (int k0 = 0; k0 < CNT; k0 += BATCH) {
+    const uint16_t* gp[BATCH];
+    #pragma unroll
+    for (int kb = 0; kb < BATCH; ++kb) {
+        const int i = first + k0 + kb;                   // wave-uniform transfer index in the round
+        const int j = i / Gm::XFER_PER_TILE;
+        const int ii = i % Gm::XFER_PER_TILE;
+        const TileSrc src = tile_src(min(round_first_tile + j, n_tiles - 1));
+        const bool isv = ii >= Gm::KB_PER_TILE;
+        const int blk = isv ? ii - Gm::KB_PER_TILE : ii;
+        const int row = blk * Gm::ROWS_PER_KB + rsub;    // key within the tile
+        const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+        const int tb = src.t0 + blk * Gm::ROWS_PER_KB;   // first key of this transfer (uniform)
+        if (src.tree) {
+            // tree tile: node rows, clamped to the last node
+            const int t = min(src.t0 + row, src.limit - 1);
+            gp[kb] = (isv ? vt : kt) + (((long)b * N + t) * Hkv + kvh) * D + c * 8;
+        } else if (src.t0 + kKeyTile <= src.limit) {
+            // full prefix tile: the transfer's 1 KB lies in one page; page base in
+            // scalar registers, lane part = row in page and chunk
+            const int page = __builtin_amdgcn_readfirstlane(s_pages[(tb >> 4) - p_begin]);
+            const long pbase = ((long)page * Hkv + kvh) * (kPage * D) + (long)(tb & 15) * D;
+            gp[kb] = (isv ? vp : kp) + pbase + rsub * D + c * 8;
+        } else {
+            // the tile that crosses the end of the prefix: keys past it read the
+            // tile's first key instead (valid and finite; the softmax masks them)
+            int t = src.t0 + row;
+            if (t >= src.limit) t = src.t0;
+            const int page = s_pages[(t >> 4) - p_begin];
+            gp[kb] = (isv ? vp : kp) + (((long)page * Hkv + kvh) * kPage + (t & 15)) * D + c * 8;
+        }
+    }
+    #pragma unroll
+    for (int kb = 0; kb < BATCH; ++kb) {
+        const int i = first + k0 + kb;
+        const int j = i / Gm::XFER_PER_TILE, ii = i % Gm::XFER_PER_TILE;
+        dma16(__builtin_amdgcn_readfirstlane(buf + j * Gm::BUF_BYTES + ii * 1024), gp[kb]);
+    }
+    }
+}
+
+// Wait until at most `pending` later rounds of this wave's transfers are in flight.
+template <int DPR>
+__device__ __forceinline__ void wait_rounds(int pending) {
+    if (pending >= 2) wait_vm<2 * DPR>();
+    else if (pending == 1) wait_vm<DPR>();
+    else wait_vm<0>();
+}
+
+// The 256-bit ancestor bitset of a lane's node, as a register vector (a
+// variable index into it selects between registers instead of spilling).
+typedef unsigned long long u64x4 __attribute__((ext_vector_type(4)));
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 ds_read_tr(const char* lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_ptr));
+}
+
+// Running state of one wave: 32 query rows, one lane pair per row.
 template <int D>
-__device__ __forceinline__ long key_elem(const AttnArgs& a, const TileSrc& src, int key, int b, int kvh,
-                                         int p_begin, const int* s_pages) {
-    const int t = src.t0 + key;
-    if (t >= src.limit) return -1;
-    if (src.tree) return (((long)b * a.N + t) * a.Hkv + kvh) * D;
-    const int page = s_pages[(t >> 4) - p_begin];
-    return (((long)page * a.Hkv + kvh) * kPage + (t & 15)) * D;
-}
+struct RowState {
+    f32x16 o[D / 32];    // O^T accumulators: lane = row, register = d
+    float m;             // reference max (log2 units), equal in both half-waves
+    float l;             // partial sum of this half-wave's keys
+};
 
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const TileSrc& src, int b, int kvh, int p_begin,
-                                          const int* s_pages, Stage<D, NW>& st) {
-    using TL = Tile<D, NW>;
-    const uint16_t* kb = src.tree ? a.kt : a.kp;
-    const uint16_t* vb = src.tree ? a.vt : a.vp;
-    const int tid = threadIdx.x;
+// Multiply one 64-key tile into a wave's running state.
+template <int D>
+__device__ __forceinline__ void tile_product(RowState<D>& st, const char* kbuf, const char* vbuf,
+                                             const bf16x8* qreg, const TileSrc& src, u64x4 ancw,
+                                             int N, float scale_log2, const int* v_off, int hf, int l32) {
+    using Gm = Geo<D>;
+    constexpr int DCH = D / 16;
+    constexpr int DT = D / 32;
+    const float NEG = -__builtin_inff();
+    // S^T = K Q^T for two 32-key halves
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
     #pragma unroll
-    for (int i = 0; i < TL::KCH; ++i) {
-        const int id = tid + i * TL::T;
-        const int key = id / TL::CPR, c = id % TL::CPR;
-        const long e = key_elem<D>(a, src, key, b, kvh, p_begin, s_pages);
-        st.k[i] = e >= 0 ? ld16(kb + e + c * 8) : u32x4{0, 0, 0, 0};
-    }
-    #pragma unroll
-    for (int i = 0; i < TL::VU; ++i) {
-        const int uid = tid + i * TL::T;
-        const int kg = uid / TL::CPR, dc = uid % TL::CPR;
+    for (int c = 0; c < DCH; ++c) {
         #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            long e = -1;
-            if (uid < TL::VUNITS) e = key_elem<D>(a, src, 4 * kg + j, b, kvh, p_begin, s_pages);
-            st.v[i][j] = e >= 0 ? ld16(vb + e + dc * 8) : u32x4{0, 0, 0, 0};
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int key = h2 * 32 + l32;
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + key * Gm::ROW_BYTES +
+                                                               (((2 * c + hf) ^ swz_k<D>(key)) << 4));
+            sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[c], sacc[h2], 0, 0, 0);
+        }
+    }
+    // register r of half h2 holds key h2*32 + 8*(r/4) + 4*hf + r%4 of the tile
+    if (src.tree) {
+        const int tt = src.t0 / kKeyTile;
+        const int left = N - src.t0;
+        uint64_t mw = ancw[tt];
+        if (left < 64) mw &= (1ull << left) - 1ull;
+        mw >>= 4 * hf;
+        const uint32_t lo = (uint32_t)mw, hi = (uint32_t)(mw >> 32);
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int sh = 8 * (r >> 2) + (r & 3);
+            if (!((lo >> sh) & 1u)) sacc[0][r] = NEG;
+            if (!((hi >> sh) & 1u)) sacc[1][r] = NEG;
+        }
+    } else if (src.t0 + kKeyTile > src.limit) {
+        const int nvalid = src.limit - src.t0 - 4 * hf;
+        #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + (r & 3);
+            if (kk >= nvalid) sacc[0][r] = NEG;
+            if (kk + 32 >= nvalid) sacc[1][r] = NEG;
+        }
+    }
+    // online softmax (log2 domain), lazy rescale
+    float mx = NEG;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    // move the reference max only when some row's max grew by more than 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.f)) {
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // m = -inf -> 0
+        st.l *= alpha;
+        #pragma unroll
+        for (int i = 0; i < DT; ++i) st.o[i] *= alpha;
+        st.m = m_new;
+    }
+    const float m_use = (st.m == NEG) ? 0.f : st.m;
+    // the row sum adds the bf16-rounded weights that the P.V product uses, two
+    // per v_dot2_f32_bf16
+    float rs = 0.f;
+    uint32_t pk[2][8];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    #pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        #pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r], scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r + 1], scale_log2, -m_use));
+            pk[h2][r >> 1] = pack_bf16x2(p0, p1);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[h2][r >> 1]), ones, rs, false);
+        }
+    }
+    st.l += rs;
+    // O^T += V^T P^T, 16 keys per step (two transposing reads give the 8 keys of a lane)
+    #pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const int h2 = kc >> 1, o4 = (kc & 1) * 4;
+        const u32x4 pw = {pk[h2][o4], pk[h2][o4 + 1], pk[h2][o4 + 2], pk[h2][o4 + 3]};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const char* vp0 = vbuf + v_off[dt] + kc * 16 * Gm::ROW_BYTES;
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, ds_read_tr(vp0));
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, ds_read_tr(vp0 + 8 * Gm::ROW_BYTES));
+            const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb, st.o[dt], 0, 0, 0);
         }
     }
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void store_tile(char* buf, const Stage<D, NW>& st) {
-    using TL = Tile<D, NW>;
-    const int tid = threadIdx.x;
-    #pragma unroll
-    for (int i = 0; i < TL::KCH; ++i) {
-        const int id = tid + i * TL::T;
-        const int key = id / TL::CPR, c = id % TL::CPR;
-        *reinterpret_cast<u32x4*>(buf + k_off<D>(key, c)) = st.k[i];
-    }
-    char* vbuf = buf + TL::K_BYTES;
-    #pragma unroll
-    for (int i = 0; i < TL::VU; ++i) {
-        const int uid = tid + i * TL::T;
-        if (uid >= TL::VUNITS) continue;
-        const int kg = uid / TL::CPR, dc = uid % TL::CPR;
-        // keys 4kg..4kg+3 go to positions 16*(kg/4) + 4*qq, with the two middle
-        // 4-key groups of each 16-key block swapped (matches the P^T registers)
-        const int q4 = kg & 3;
-        const int qq = ((q4 & 1) << 1) | (q4 >> 1);
-        const int chunk = 2 * (kg >> 2) + (qq >> 1);
-        const int half = (qq & 1) * 8;
-        #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const uint32_t r0 = st.v[i][0][m], r1 = st.v[i][1][m], r2 = st.v[i][2][m], r3 = st.v[i][3][m];
-            const int d0 = 8 * dc + 2 * m;
-            // even element of the pair: low halves; odd: high halves
-            u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
-            u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
-            *reinterpret_cast<u32x2*>(vbuf + vt_off(d0, chunk) + half) = lo;
-            *reinterpret_cast<u32x2*>(vbuf + vt_off(d0 + 1, chunk) + half) = hi;
-        }
-    }
+// Byte offset of float4 chunk c of row r in a [rows][D] fp32 LDS array,
+// chunk-swizzled so that 8 consecutive rows at one chunk hit distinct banks.
+template <int D>
+__device__ __forceinline__ int merge_off(int r, int c) {
+    return r * (D * 4) + ((c ^ (r & 7)) << 4);
 }
 
-__device__ __forceinline__ uint64_t pick_word(const uint64_t w[4], int i) {
-    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
-}
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) {
-    using TL = Tile<D, NW>;
-    constexpr int RB = NW * 32;
-    constexpr int DCH = D / 16;     // k-steps of the QK product
-    constexpr int DT = D / 32;      // 32-wide d tiles of O^T
-    __shared__ __attribute__((aligned(16))) char lds[2][TL::BUF_BYTES];
+template <int D, int RW, int KW>
+__global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
+    using Gm = Geo<D>;
+    constexpr int NW = RW * KW;
+    constexpr int T = NW * 64;
+    constexpr int RB = RW * 32;
+    constexpr int DCH = D / 16;                      // k-steps of the QK product
+    constexpr int DT = D / 32;                       // 32-wide d tiles of O^T
+    constexpr int RING_R = kRing / KW;               // rounds the ring holds
+    constexpr int DPR = KW * Gm::XFER_PER_TILE / NW; // transfers per wave per round
+    static_assert(kRing % KW == 0 && (KW * Gm::XFER_PER_TILE) % NW == 0, "bad wave split");
+    static_assert(KW == 1 || KW * RB * D * 4 <= kRing * Gm::BUF_BYTES, "key-group merge must fit the ring");
+    __shared__ __attribute__((aligned(1024))) char ring[kRing * Gm::BUF_BYTES];
     __shared__ int s_pages[kMaxPagesPerSplit];
+    __shared__ float s_ml[KW][RB][2];
     __shared__ unsigned long long s_union[kAncWords];
     __shared__ int s_last;
 
@@ -200,27 +335,28 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
     const int b = t1 / a.Hkv;
     const int item = (b * a.Hkv + kvh) * a.nrb + rb;
 
-    int L = a.prefix_len[b];
-    bool bad = (L < 0 || L > a.max_prefix);
-    if (bad) L = 0;
-    const int npages = (L + kPage - 1) / kPage;
-    int n_act = (npages + a.pps - 1) / a.pps;
-    if (n_act < 1) n_act = 1;
-    if (s >= n_act) return;                                   // uniform: the whole workgroup leaves
-    const int p_begin = s * a.pps;
-    const int p_end = min(npages, p_begin + a.pps);
-    const int tok_begin = p_begin * kPage;
-    const int tok_end = min(L, p_end * kPage);
-    const bool has_tree = (s == n_act - 1);
-
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rw = w % RW, kw = w / RW;
     const int hf = lane >> 5, l32 = lane & 31;
-    const int row = rb * RB + w * 32 + l32;
+    const int rloc = rw * 32 + l32;                 // row within the row block
+    const int row = rb * RB + rloc;
     const bool row_ok = row < a.rows;
     const int node = row_ok ? row / a.G : 0;
     const int head = kvh * a.G + (row_ok ? row % a.G : 0);
 
-    // ---- Q rows of this wave -> registers (B operand: lane = row, 8 d values per k-step)
+    // ---- every global read of the set-up is issued at once: the prefix length,
+    // this split's block-table entries (the page range does not depend on the
+    // length), the wave's Q rows and the rows' ancestor words
+    constexpr int PPT = (kMaxPagesPerSplit + T - 1) / T;
+    const int p_begin = s * a.pps;
+    const int p_avail = min(a.pps, a.max_pages - p_begin);
+    int L = a.prefix_len[b];
+    int pid[PPT];
+    #pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int i = tid + k * T;
+        pid[k] = (i < p_avail) ? a.block_table[(long)b * a.max_pages + p_begin + i] : 0;
+    }
     bf16x8 qreg[DCH];
     {
         const uint16_t* qp = a.q + (((long)b * a.N + node) * a.Hq + head) * D + 8 * hf;
@@ -230,26 +366,43 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
             qreg[c] = __builtin_bit_cast(bf16x8, v);
         }
     }
-    uint64_t ancw[kAncWords] = {0, 0, 0, 0};
-    if (tid < kAncWords) s_union[tid] = 0;
-    __syncthreads();
-    if (has_tree && row_ok) {
+    u64x4 ancw = {0, 0, 0, 0};
+    if (row_ok) {
         #pragma unroll
         for (int k = 0; k < kAncWords; ++k) ancw[k] = a.anc[((long)b * a.N + node) * kAncWords + k];
-        if (row % a.G == 0) {
-            #pragma unroll
-            for (int k = 0; k < kAncWords; ++k)
-                if (ancw[k]) atomicOr(&s_union[k], (unsigned long long)ancw[k]);
-        }
+    }
+
+    bool bad = (L < 0 || L > a.max_prefix);
+    if (bad) L = 0;
+    const int npages = (L + kPage - 1) / kPage;
+    int n_act = (npages + a.pps - 1) / a.pps;
+    if (n_act < 1) n_act = 1;
+    if (s >= n_act) return;                                   // uniform: the whole workgroup leaves
+    const int p_end = min(npages, p_begin + a.pps);
+    const int tok_begin = p_begin * kPage;
+    const int tok_end = min(L, p_end * kPage);
+    const bool has_tree = (s == n_act - 1);
+    if (!has_tree) ancw = u64x4{0, 0, 0, 0};
+
+    if (tid < kAncWords) s_union[tid] = 0;
+    __syncthreads();
+    if (has_tree && row_ok && kw == 0 && row % a.G == 0) {
+        #pragma unroll
+        for (int k = 0; k < kAncWords; ++k)
+            if (ancw[k]) atomicOr(&s_union[k], (unsigned long long)ancw[k]);
     }
     int my_bad = 0;
-    for (int i = tid; i < p_end - p_begin; i += TL::T) {
-        int pid = a.block_table[(long)b * a.max_pages + p_begin + i];
-        if (pid < 0 || pid >= a.num_pages) {
-            my_bad = 1;
-            pid = 0;
+    #pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int i = tid + k * T;
+        if (i < p_end - p_begin) {
+            int v = pid[k];
+            if (v < 0 || v >= a.num_pages) {
+                my_bad = 1;
+                v = 0;
+            }
+            s_pages[i] = v;
         }
-        s_pages[i] = pid;
     }
     bad = __syncthreads_or(my_bad) || bad;
 
@@ -265,8 +418,9 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
         }
     }
     const int n_tiles = n_pre + n_tree;
-
-    auto tile_src = [&](int it) {
+    const int n_rounds = (n_tiles + KW - 1) / KW;
+    const int N = a.N;
+    auto tile_src = [=](int it) {
         TileSrc src;
         if (it < n_pre) {
             src.tree = false;
@@ -275,148 +429,182 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
         } else {
             src.tree = true;
             src.t0 = ((tree_list >> (2 * (it - n_pre))) & 3) * kKeyTile;
-            src.limit = a.N;
+            src.limit = N;
         }
         return src;
     };
 
-    f32x16 oacc[DT];
+    const uint32_t ring0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)ring);
+    const uint16_t* const g_kp = a.kp;
+    const uint16_t* const g_vp = a.vp;
+    const uint16_t* const g_kt = a.kt;
+    const uint16_t* const g_vt = a.vt;
+    const int Hkv = a.Hkv;
+    const float scale_log2 = a.scale_log2;
+
+    // per-lane LDS offsets (within one V tile) of the transposing PV operand reads:
+    // in 16-lane group g16, lane x reads key 16*kc + 8*rd + 4*hf + x/4 at
+    // d = 32*dt + 16*(g16&1) + 4*(x&3); it receives keys 4*hf + {0..3} (+8*rd)
+    // at d = 32*dt + lane%32, which is the A operand of the 32x32x16 product
+    const int x16 = lane & 15, g16 = lane >> 4;
+    int v_off[DT];
     #pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+    for (int dt = 0; dt < DT; ++dt) {
+        const int key = 4 * hf + (x16 >> 2);
+        const int d = 32 * dt + 16 * (g16 & 1) + 4 * (x16 & 3);
+        v_off[dt] = key * Gm::ROW_BYTES + (((d >> 3) ^ swz_v<D>(key)) << 4) + ((d >> 2) & 1) * 8;
+    }
+
+    RowState<D> st;
+    #pragma unroll
+    for (int i = 0; i < DT; ++i) st.o[i] = f32x16{};
     const float NEG = -__builtin_inff();
-    float m_run = NEG;
-    float l_run = 0.f;
+    st.m = NEG;
+    st.l = 0.f;
 
-    Stage<D, NW> stage;
-    if (n_tiles > 0) {
-        load_tile<D, NW>(a, tile_src(0), b, kvh, p_begin, s_pages, stage);
-        store_tile<D, NW>(lds[0], stage);
+    // every load the compiler issued (Q, anc, page table) has landed: from here on
+    // the only vector-memory traffic is the tile ring, counted by hand
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if constexpr (RING_R >= 2) {
+        // prologue: RING_R - 1 rounds in flight
+        #pragma unroll
+        for (int p = 0; p < RING_R - 1; ++p)
+            if (p < n_rounds)
+                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, p * KW, n_tiles, b, kvh, p_begin, s_pages,
+                                    ring0 + p * KW * Gm::BUF_BYTES, w * DPR, lane);
     }
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const TileSrc src = tile_src(it);
-        if (it + 1 < n_tiles) load_tile<D, NW>(a, tile_src(it + 1), b, kvh, p_begin, s_pages, stage);
-        const char* kbuf = lds[it & 1];
-        const char* vbuf = kbuf + TL::K_BYTES;
-
-        // S^T = K Q^T for two 32-key halves
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
-        #pragma unroll
-        for (int c = 0; c < DCH; ++c) {
-            #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int key = h2 * 32 + l32;
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + k_off<D>(key, 2 * c + hf));
-                sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[c], sacc[h2], 0, 0, 0);
-            }
+    for (int r = 0; r < n_rounds; ++r) {
+        if constexpr (RING_R >= 2) {
+            wait_rounds<DPR>(min(n_rounds - 1 - r, RING_R - 2));
+            __syncthreads();      // round r is in LDS for every wave; the buffers of round r-1 are free
+            if (r + RING_R - 1 < n_rounds)
+                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, (r + RING_R - 1) * KW, n_tiles, b, kvh, p_begin, s_pages,
+                                    ring0 + ((r + RING_R - 1) % RING_R) * KW * Gm::BUF_BYTES, w * DPR, lane);
+        } else {
+            __syncthreads();      // every wave is done with the previous round
+            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, p_begin, s_pages, ring0, w * DPR, lane);
+            wait_vm<0>();
+            __syncthreads();
         }
-        // register r of half h2 holds key h2*32 + 8*(r/4) + 4*hf + r%4 of the tile
-        if (src.tree) {
-            const int tt = src.t0 / kKeyTile;
-            const int left = a.N - src.t0;
-            uint64_t mw = pick_word(ancw, tt);
-            if (left < 64) mw &= (1ull << left) - 1ull;
-            mw >>= 4 * hf;
-            const uint32_t lo = (uint32_t)mw, hi = (uint32_t)(mw >> 32);
-            #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int sh = 8 * (r >> 2) + (r & 3);
-                if (!((lo >> sh) & 1u)) sacc[0][r] = NEG;
-                if (!((hi >> sh) & 1u)) sacc[1][r] = NEG;
-            }
-        } else if (src.t0 + kKeyTile > src.limit) {
-            const int nvalid = src.limit - src.t0 - 4 * hf;
-            #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = 8 * (r >> 2) + (r & 3);
-                if (kk >= nvalid) sacc[0][r] = NEG;
-                if (kk + 32 >= nvalid) sacc[1][r] = NEG;
-            }
+        const int it = r * KW + kw;
+        if (it < n_tiles) {
+            const char* kbuf = ring + ((r % RING_R) * KW + kw) * Gm::BUF_BYTES;
+            tile_product<D>(st, kbuf, kbuf + Gm::TILE_BYTES, qreg, tile_src(it), ancw, N, scale_log2, v_off, hf, l32);
         }
-        // online softmax (log2 domain)
-        float mx = NEG;
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        const float m_use = (m_new == NEG) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float rs = 0.f;
-        uint32_t pk[2][8];
-        #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r], a.scale_log2, -m_use));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r + 1], a.scale_log2, -m_use));
-                rs += p0 + p1;
-                pk[h2][r >> 1] = pack_bf16x2(p0, p1);
-            }
-        }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        #pragma unroll
-        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-
-        // O^T += V^T P^T, 16 keys per step
-        #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const int h2 = kc >> 1, o4 = (kc & 1) * 4;
-            const u32x4 pw = {pk[h2][o4], pk[h2][o4 + 1], pk[h2][o4 + 2], pk[h2][o4 + 3]};
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-            #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 32 + l32;
-                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vbuf + vt_off(d, 2 * kc + hf));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[dt], 0, 0, 0);
-            }
-        }
-        if (it + 1 < n_tiles) store_tile<D, NW>(lds[(it + 1) & 1], stage);
-        __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float NANF = __builtin_nanf("");
     const float LN2 = 0.69314718055994530942f;
+    float* mo = reinterpret_cast<float*>(ring);      // key-group merge area (reuses the ring)
 
-    if (n_act == 1) {
-        if (row_ok) {
-            const float inv = bad ? NANF : 1.f / l_tot;
-            uint16_t* op = a.out + (((long)b * a.N + node) * a.Hq + head) * D + 4 * hf;
-            #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
+    // ---- one row block's result, as (m, l, unnormalised O) per row
+    if constexpr (KW == 1) {
+        const float l_tot = st.l + __shfl_xor(st.l, 32);
+        if (n_act == 1) {
+            if (row_ok) {
+                const float inv = bad ? NANF : 1.f / l_tot;
+                uint16_t* op = a.out + (((long)b * a.N + node) * a.Hq + head) * D + 4 * hf;
                 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const u32x2 v = {pack_bf16x2(oacc[dt][4 * rq] * inv, oacc[dt][4 * rq + 1] * inv),
-                                     pack_bf16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = v;
+                for (int dt = 0; dt < DT; ++dt) {
+                    #pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const u32x2 v = {pack_bf16x2(st.o[dt][4 * rq] * inv, st.o[dt][4 * rq + 1] * inv),
+                                         pack_bf16x2(st.o[dt][4 * rq + 2] * inv, st.o[dt][4 * rq + 3] * inv)};
+                        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = v;
+                    }
                 }
+                if (a.lse && hf == 0)
+                    a.lse[((long)b * a.N + node) * a.Hq + head] = bad ? NANF : (st.m + __log2f(l_tot)) * LN2;
             }
-            if (a.lse && hf == 0)
-                a.lse[((long)b * a.N + node) * a.Hq + head] = bad ? NANF : (m_run + __log2f(l_tot)) * LN2;
+            return;
         }
-        return;
-    }
-
-    // ---- several splits: publish this split's partial result
-    {
-        const long pr = ((long)item * a.splits + s) * RB + (row - rb * RB);
-        float* po = a.part_o + pr * D + 4 * hf;
+        const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rloc;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const f32x4 v = {oacc[dt][4 * rq], oacc[dt][4 * rq + 1], oacc[dt][4 * rq + 2], oacc[dt][4 * rq + 3]};
-                *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * rq) = v;
+                const f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
+                st_agent16(ro, (pr * D + dt * 32 + 8 * rq + 4 * hf) * 4, v);
             }
         }
         if (hf == 0) {
-            a.part_ml[pr * 2 + 0] = bad ? NANF : m_run;
-            a.part_ml[pr * 2 + 1] = bad ? NANF : l_tot;
+            const u32x2 ml = {__float_as_uint(bad ? NANF : st.m), __float_as_uint(bad ? NANF : l_tot)};
+            st_agent8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
+        }
+    } else {
+        // merge the KW key groups through LDS
+        const float l_tot = st.l + __shfl_xor(st.l, 32);
+        __syncthreads();                               // every wave is done with the ring
+        {
+            char* mk = reinterpret_cast<char*>(mo) + kw * RB * D * 4;
+            #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                #pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
+                    *reinterpret_cast<f32x4*>(mk + merge_off<D>(rloc, (dt * 32 + 8 * rq + 4 * hf) >> 2)) = v;
+                }
+            }
+            if (hf == 0) {
+                s_ml[kw][rloc][0] = st.m;
+                s_ml[kw][rloc][1] = l_tot;
+            }
+        }
+        __syncthreads();
+        constexpr int TPR = T / RB;                 // threads per row
+        constexpr int CPT = D / 4 / TPR;            // float4 chunks per thread
+        const int rl = tid / TPR, part = tid % TPR;
+        const int grow = rb * RB + rl;
+        float M = NEG;
+        #pragma unroll
+        for (int k = 0; k < KW; ++k) M = fmaxf(M, s_ml[k][rl][0]);
+        const float M_use = (M == NEG) ? 0.f : M;
+        float wk[KW];
+        float Ls = 0.f;
+        #pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            wk[k] = __builtin_amdgcn_exp2f(s_ml[k][rl][0] - M_use);
+            Ls += wk[k] * s_ml[k][rl][1];
+        }
+        f32x4 acc[CPT];
+        #pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int k = 0; k < KW; ++k)
+                acc[c] += wk[k] * *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(mo) + k * RB * D * 4 +
+                                                                  merge_off<D>(rl, part * CPT + c));
+        }
+        if (n_act == 1) {
+            if (grow < a.rows) {
+                const int gnode = grow / a.G, ghead = kvh * a.G + grow % a.G;
+                const float inv = bad ? NANF : 1.f / Ls;
+                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * CPT * 4;
+                #pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
+                                     pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+                    *reinterpret_cast<u32x2*>(op + 4 * c) = v;
+                }
+                if (a.lse && part == 0)
+                    a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = bad ? NANF : (M + __log2f(Ls)) * LN2;
+            }
+            return;
+        }
+        const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rl;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
+        #pragma unroll
+        for (int c = 0; c < CPT; ++c) st_agent16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4, acc[c]);
+        if (part == 0) {
+            const u32x2 ml = {__float_as_uint(bad ? NANF : M), __float_as_uint(bad ? NANF : Ls)};
+            st_agent8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
         }
     }
-    __threadfence();
+
+    // ---- several splits: this split's partial is published; the last one merges
+    wait_own_stores();
     __syncthreads();
     if (tid == 0) {
         const int old = arrive(&a.counters[item]);
@@ -425,47 +613,60 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
-    // ---- last split to finish: merge all splits of this row block, in split order
     {
-        constexpr int TPR = TL::T / RB;            // threads per row (2)
-        constexpr int DPT = D / TPR;               // d values per thread
+        constexpr int TPR = T / RB;                // threads per row
+        constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread
+        constexpr int SB = (32 / CPT) > 1 ? (32 / CPT) : 1;   // splits per batch: <= 32 float4 in flight
         const int rl = tid / TPR, part = tid % TPR;
         const int grow = rb * RB + rl;
-        if (grow < a.rows) {
-            const long base = (long)item * a.splits * RB + rl;   // + sp * RB
-            float M = NEG;
-            for (int sp = 0; sp < n_act; ++sp) M = fmaxf(M, a.part_ml[(base + (long)sp * RB) * 2]);
-            const float M_use = (M == NEG) ? 0.f : M;
-            float acc[DPT];
+        const uint32_t base = (uint32_t)item * a.splits * RB + rl;   // + sp * RB
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
+        const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
+        // one batch of loads (every split's m, l and O slice) per SB splits, merged
+        // with a running max so no pass has to wait for another
+        float M = NEG;
+        f32x4 acc[CPT];
+        #pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float Ls = 0.f;
+        for (int sp0 = 0; sp0 < n_act; sp0 += SB) {
+            f32x4 v[SB][CPT];
+            u32x2 ml[SB];
             #pragma unroll
-            for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
-            float Ls = 0.f;
-            for (int sp = 0; sp < n_act; ++sp) {
-                const long pr = base + (long)sp * RB;
-                const float wgt = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - M_use);
-                Ls += wgt * a.part_ml[pr * 2 + 1];
-                const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + pr * D + part * DPT);
+            for (int j = 0; j < SB; ++j) {
+                const uint32_t pr = base + (uint32_t)min(sp0 + j, n_act - 1) * RB;
                 #pragma unroll
-                for (int i = 0; i < DPT / 4; ++i) {
-                    const f32x4 v = src[i];
-                    acc[4 * i] += wgt * v[0];
-                    acc[4 * i + 1] += wgt * v[1];
-                    acc[4 * i + 2] += wgt * v[2];
-                    acc[4 * i + 3] += wgt * v[3];
-                }
+                for (int c = 0; c < CPT; ++c) v[j][c] = ld_agent16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4);
+                ml[j] = ld_agent8(rml, pr * 8);
             }
+            float mb = NEG;
+            #pragma unroll
+            for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));   // clamped repeats: no change
+            const float Mn = fmaxf(M, mb);
+            const float Mn_use = (Mn == NEG) ? 0.f : Mn;
+            const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                      // M = -inf -> 0
+            Ls *= sc;
+            #pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] *= sc;
+            #pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const float wgt = (sp0 + j < n_act) ? __builtin_amdgcn_exp2f(__uint_as_float(ml[j][0]) - Mn_use) : 0.f;
+                Ls += wgt * __uint_as_float(ml[j][1]);
+                #pragma unroll
+                for (int c = 0; c < CPT; ++c) acc[c] += wgt * v[j][c];
+            }
+            M = Mn;
+        }
+        if (grow < a.rows) {
             const int gnode = grow / a.G, ghead = kvh * a.G + grow % a.G;
             const float inv = 1.f / Ls;
-            uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * DPT;
+            uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * CPT * 4;
             #pragma unroll
-            for (int i = 0; i < DPT / 8; ++i) {
-                const u32x4 v = {pack_bf16x2(acc[8 * i] * inv, acc[8 * i + 1] * inv),
-                                 pack_bf16x2(acc[8 * i + 2] * inv, acc[8 * i + 3] * inv),
-                                 pack_bf16x2(acc[8 * i + 4] * inv, acc[8 * i + 5] * inv),
-                                 pack_bf16x2(acc[8 * i + 6] * inv, acc[8 * i + 7] * inv)};
-                *reinterpret_cast<u32x4*>(op + 8 * i) = v;
+            for (int c = 0; c < CPT; ++c) {
+                const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
+                                 pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+                *reinterpret_cast<u32x2*>(op + 4 * c) = v;
             }
             if (a.lse && part == 0) a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
         }
@@ -475,7 +676,7 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attn_bf16_kernel(AttnArgs a) 
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
-    int nw, rb, nrb, items, splits, pps;
+    int rw, kw, rb, nrb, items, splits, pps;
     long grid;
     size_t off_cnt, off_ml, off_o, bytes;
 };
@@ -491,15 +692,22 @@ static int env_int(const char* name, int dflt) {
 AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     AttnPlanBf16 p{};
     const long rows = (long)(s.Hq / s.Hkv) * s.N;
-    p.nw = rows <= 64 ? 2 : 4;
-    p.rb = 32 * p.nw;
+    // few rows -> key groups keep several tiles in flight per workgroup
+    if (rows <= 32) { p.rw = 1; p.kw = 4; }
+    else if (rows <= 64) { p.rw = 2; p.kw = 2; }
+    else if (rows <= 128) { p.rw = 4; p.kw = 2; }
+    else { p.rw = 8; p.kw = 1; }
+    p.rb = 32 * p.rw;
     p.nrb = (int)((rows + p.rb - 1) / p.rb);
     p.items = s.B * s.Hkv * p.nrb;
     const int max_pages = (max_prefix + kPage - 1) / kPage;
-    // enough workgroups to cover 256 CUs several times; splits of whole 64-key tiles
-    const int target = env_int("JF_TARGET_WG", 1024);
+    // one workgroup per CU (the LDS ring takes most of it): aim at filling 256 CUs
+    const int target = env_int("JF_TARGET_WG", 256);
+    // at least one full round of tiles per split
+    const int min_pages = 4 * p.kw;
     int splits = p.items > 0 ? (target + p.items - 1) / p.items : 1;
-    const int max_splits = max_pages > 0 ? (max_pages + 3) / 4 : 1;
+    int max_splits = max_pages > 0 ? (max_pages + min_pages - 1) / min_pages : 1;
+    if (max_splits > kMaxSplits) max_splits = kMaxSplits;
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
     const int forced = env_int("JF_SPLITS", 0);
     if (forced > 0) splits = forced < max_splits ? forced : max_splits;
@@ -510,6 +718,17 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     p.splits = splits;
     p.pps = pps;
     p.grid = (long)p.items * splits;
+    // split partials are addressed with 32-bit buffer offsets
+    while (splits > 1 && (size_t)p.items * splits * p.rb * s.D * 4 >= (size_t)0xffffff00u) {
+        splits = (splits + 1) / 2;
+        pps = (max_pages + splits - 1) / splits;
+        pps = (pps + 3) / 4 * 4;
+        if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+        splits = (max_pages + pps - 1) / pps;
+        p.splits = splits;
+        p.pps = pps;
+        p.grid = (long)p.items * splits;
+    }
     if (splits > 1) {
         p.off_cnt = 0;
         p.off_ml = align256((size_t)p.items * 4);
@@ -519,10 +738,18 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     return p;
 }
 
-template <int D, int NW>
+template <int D, int RW, int KW>
 static hipError_t launch_bf16_t(const AttnArgs& a, long grid, hipStream_t stream) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, RW, KW>), dim3((unsigned)grid), dim3(RW * KW * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bf16_d(const AttnPlanBf16& p, const AttnArgs& a, hipStream_t stream) {
+    if (p.rw == 1) return launch_bf16_t<D, 1, 4>(a, p.grid, stream);
+    if (p.rw == 2) return launch_bf16_t<D, 2, 2>(a, p.grid, stream);
+    if (p.rw == 4) return launch_bf16_t<D, 4, 2>(a, p.grid, stream);
+    return launch_bf16_t<D, 8, 1>(a, p.grid, stream);
 }
 
 hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
@@ -546,6 +773,8 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.counters = p.splits > 1 ? reinterpret_cast<int*>(ws + p.off_cnt) : nullptr;
     a.part_ml = p.splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
     a.part_o = p.splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+    a.part_ml_bytes = (uint32_t)(p.off_o - p.off_ml);
+    a.part_o_bytes = (uint32_t)(p.bytes - p.off_o);
     a.B = s.B;
     a.N = s.N;
     a.Hq = s.Hq;
@@ -559,8 +788,7 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.splits = p.splits;
     a.pps = p.pps;
     a.scale_log2 = s.sm_scale * 1.44269504088896340736f;
-    if (s.D == 128) return p.nw == 2 ? launch_bf16_t<128, 2>(a, p.grid, stream) : launch_bf16_t<128, 4>(a, p.grid, stream);
-    return p.nw == 2 ? launch_bf16_t<64, 2>(a, p.grid, stream) : launch_bf16_t<64, 4>(a, p.grid, stream);
+    return s.D == 128 ? launch_bf16_d<128>(p, a, stream) : launch_bf16_d<64>(p, a, stream);
 }
 
 size_t attention_bf16_workspace_bytes(const jf_attn_shape& s, int max_prefix) {

@@ -38,15 +38,48 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
     return xcd * q + (xcd < rem ? xcd : rem) + slot;
 }
 
-// Release this workgroup's prior global writes and bump an agent-scope
-// counter; returns the old value. Every thread must have issued a
-// __threadfence() after its own writes and the workgroup must be at a barrier.
+// Cross-workgroup hand-off (split merge, argmax merge, acceptance walk).
+//
+// MI355X has one L2 per XCD and they are not coherent with each other. A
+// result that a workgroup on another XCD will read is therefore written and
+// read with agent-scope accesses (cache policy sc1): such a store is complete
+// only once it is visible device-wide, and such a load does not hit a stale
+// line of the local L2. No cache-wide write-back or invalidate is needed:
+//   writer: agent-scope stores, wait_own_stores() in every wave, barrier,
+//           then ONE thread bumps the agent-scope counter (arrive);
+//   reader: the thread that saw the last arrival tells the workgroup through
+//           LDS and a barrier; the workgroup reads with agent-scope loads.
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ int arrive(int* counter) {
-    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void reset_counter(int* counter) {
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kAgentScope = 16;   // buffer-instruction cache policy: sc1 (device scope)
+
+// Raw buffer over `bytes` bytes at `base` (out-of-range accesses read 0 and drop writes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAgentScope);
+}
+
+__device__ __forceinline__ f32x4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAgentScope));
+}
+
+__device__ __forceinline__ void st_agent8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kAgentScope);
+}
+
+__device__ __forceinline__ u32x2 ld_agent8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAgentScope);
 }
 
 }  // namespace jf
