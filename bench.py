@@ -15,11 +15,23 @@ back-to-back launches of that kernel alone, on the stream it runs on), the
 attention roofline fraction, the budget-256 workload (batch 8, 256-node
 best-first trees, prefixes U[1024, 4096]) as `budget256`, and the fp64 CPU
 oracle on a bounded sample as `cpu_baseline`.
+
+`roofline.traffic` is the attention kernel's HBM bytes per launch from the
+FETCH_SIZE / WRITE_SIZE counter summary in profiles/ (each counter scaled by
+what it reads for a plain 256 MiB copy in the same run); it is null when the
+kernel sources have changed since those counters were taken. The summary is
+made by:
+    rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- python bench.py --profile-steps 20
+    rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- python bench.py --profile-steps 20
+    python bench.py --summarize-pmc F W
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -32,6 +44,9 @@ import torch
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MALL_BYTES = 256 << 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20          # counter calibration: plain copy, reads and writes this much
+ATTN_KERNEL = "tree_attn_bf16_kernel"
 
 
 def log(*a):
@@ -49,8 +64,105 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of graph replay")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="run only this many eager steps of each kernel (for rocprofv3) and exit")
+                    help="run a 256 MiB copy (counter calibration), then this many eager steps, and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of --profile-steps into the traffic summary")
+    ap.add_argument("--no-long-context", action="store_true")
     return ap.parse_args()
+
+
+def source_digest():
+    """sha256 over the HIP sources and the public header (counters go stale when they change)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "tree_causal_attention_jf_amd", "csrc", "*"))) + \
+        [os.path.join(ROOT, "include", "jf_tree.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", f"{ATTN_KERNEL}_{config}_hbm_traffic.txt")
+
+
+def read_counter_csv(d, counter):
+    """{kernel name: [per-dispatch values]} for one counter of a rocprofv3 --pmc csv run."""
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert paths, f"no counter_collection.csv under {d}"
+    per = {}
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, config):
+    fetch = read_counter_csv(fetch_dir, "FETCH_SIZE")
+    write = read_counter_csv(write_dir, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024
+
+    def copy_kernel(per):
+        # the calibration copy is the only dispatch moving ~COPY_BYTES
+        cands = [(n, max(v)) for n, v in per.items() if "copy" in n.lower() or "elementwise" in n.lower()]
+        n, v = max(cands, key=lambda t: t[1])
+        return n, v
+
+    cf_name, cf = copy_kernel(fetch)
+    cw_name, cw = copy_kernel(write)
+    f_fac, w_fac = copy_kib / cf, copy_kib / cw
+    lines = [f"# HBM traffic of the tree attention kernel, workload {config}",
+             "# made by:",
+             f"#   rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
+             f"python bench.py --config {config} --profile-steps 20",
+             f"#   rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv -- "
+             f"python bench.py --config {config} --profile-steps 20",
+             f"#   python bench.py --config {config} --summarize-pmc {fetch_dir} {write_dir}",
+             f"# calibration: a {COPY_BYTES >> 20} MiB copy reads FETCH_SIZE {cf:.0f} KiB and "
+             f"WRITE_SIZE {cw:.0f} KiB per dispatch",
+             f"#   ({cf_name[:60]}); scale factors fetch {f_fac:.4f}, write {w_fac:.4f}",
+             "# kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled bytes/dispatch"]
+    attn = None
+    for name in sorted(set(fetch) & set(write)):
+        if "jf::" not in name:
+            continue
+        fv, wv = fetch[name], write[name]
+        favg, wavg = sum(fv) / len(fv), sum(wv) / len(wv)
+        scaled = favg * f_fac * 1024 + wavg * w_fac * 1024
+        lines.append(f"# {name} | {len(fv)} | {favg:.1f} | {wavg:.1f} | {scaled:.0f}")
+        if ATTN_KERNEL in name:
+            attn = (name, scaled)
+    assert attn is not None, "no attention kernel in the counter runs"
+    lines += [f"kernel: {attn[0]}",
+              f"traffic_bytes_per_launch: {attn[1]:.0f}",
+              f"fetch_factor: {f_fac:.6f}",
+              f"write_factor: {w_fac:.6f}",
+              f"source_sha256: {source_digest()}"]
+    out = traffic_file(config)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print(f"wrote {out}")
+
+
+def read_traffic(config):
+    """Bytes per launch from the committed counter summary, or None if absent or stale."""
+    path = traffic_file(config)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None, "kernel sources changed since the counters were taken"
+    return float(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
 class DeviceSet:
@@ -174,6 +286,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -199,6 +314,13 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_steps:
+        # counter calibration: a plain copy that reads and writes COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         with torch.cuda.stream(stream):
             for i in range(args.profile_steps):
                 steps[i % len(sets)]()
@@ -244,8 +366,12 @@ def main():
     log(f"[bench] per launch: mask {t_mask * 1e3:.2f} us, attention {t_attn * 1e3:.2f} us, "
         f"accept {t_acc * 1e3:.2f} us")
     achieved = nbytes / (t_attn * 1e-3) / 1e9
+    traffic, traffic_src = read_traffic(args.config)
     rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+          "frac": round(achieved / HBM_PEAK_GBS, 4),
+          "traffic": None if traffic is None else round(traffic / (t_attn * 1e-3) / 1e9, 1),
+          "traffic_bytes_per_launch": None if traffic is None else int(traffic),
+          "traffic_source": traffic_src,
           "kernel": "tree_attn_bf16_kernel", "algorithmic_bytes": nbytes, "flops": flops,
           "avg_launch_us": round(t_attn * 1e3, 3)}
     logit_bytes = wl.logits.numel() * wl.logits.element_size() if wl.logits is not None else 0
@@ -297,6 +423,37 @@ def main():
                          "hbm_GBps": round(nb2 / (t2 * 1e-3) / 1e9, 1), "flops": fl2, "algorithmic_bytes": nb2},
             "input_sets": len(sets2)}
         log(f"[bench] budget256: {t2 * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---- long context: batch 4, prefix 32768, 256-node trees; attention and acceptance timed apart
+    if not args.no_long_context:
+        log("[bench] building workload c4_bf256_32k")
+        wl4 = W.make_workload("c4_bf256_32k", 0)
+        b4 = DeviceSet(wl4)
+        sets4 = rotation_sets(wl4, b4, cap=2)
+        m4, a4, acc4, _ = make_steps(jf, wl4, sets4)
+        with torch.cuda.stream(stream):
+            for f in m4 + a4 + acc4:
+                f()
+        torch.cuda.synchronize()
+        nb4, fl4 = attention_work(wl4, b4.depth.cpu().numpy())
+        t4 = time_graph(a4, 20, stream)
+        tacc4 = time_graph(acc4, 50, stream)
+        tf4 = fl4 / (t4 * 1e-3) / 1e12
+        lb = wl4.logits.numel() * wl4.logits.element_size()
+        result["long_context"] = {
+            "workload": "c4_bf256_32k: batch 4, prefix 32768, 256-node best-first trees, 32q/8kv, d=128; "
+                        "accept over bf16 logits [4,256,151936]",
+            "tree_tokens_per_s": round(wl4.B * wl4.N / (t4 * 1e-3), 1), "attention_us": round(t4 * 1e3, 3),
+            "attention_roofline": {"bound": "mfma", "achieved": round(tf4, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf4 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "flops": fl4, "algorithmic_bytes": nb4},
+            "accept_us": round(tacc4 * 1e3, 3),
+            "accept_roofline": {"bound": "hbm", "achieved": round(lb / (tacc4 * 1e-3) / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(lb / (tacc4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "logit_bytes": lb},
+            "input_sets": len(sets4)}
+        log(f"[bench] long context: attention {t4 * 1e3:.1f} us ({tf4:.1f} TFLOP/s), accept {tacc4 * 1e3:.1f} us")
+        del sets4, b4, a4, acc4, m4
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -110,6 +110,26 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* gptr) {
                  : "memory", "m0");
 }
 
+// The same from a wave-uniform base (scalar registers) plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+// max(a, b, c) in one instruction (inputs are finite or -inf here, so no NaN
+// quieting is needed)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of a value over lanes i and i ^ 32 (swap of the two half-waves)
+__device__ __forceinline__ float max_halves(float x) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -121,64 +141,87 @@ struct TileSrc {
     int limit;     // prefix: one past the last valid token; tree: N
 };
 
+// Per-lane byte offsets, inside one page of one KV head, of the chunks a lane
+// moves in transfer kb (0 .. TPP-1) of that page: K and V differ only in the
+// swizzle. A page is TPP = 16 * ROW_BYTES / 1024 consecutive 1 KB transfers.
+template <int D>
+struct PageLanes {
+    static constexpr int TPP = kPage * Geo<D>::ROW_BYTES / 1024;
+    uint32_t k[TPP], v[TPP];
+};
+
+template <int D>
+__device__ __forceinline__ PageLanes<D> page_lanes(int lane) {
+    using Gm = Geo<D>;
+    PageLanes<D> pl;
+    const int rsub = lane / Gm::CPR, pc = lane % Gm::CPR;
+    #pragma unroll
+    for (int kb = 0; kb < PageLanes<D>::TPP; ++kb) {
+        const int row = kb * Gm::ROWS_PER_KB + rsub;     // key within the page (and, mod 16, the tile)
+        pl.k[kb] = (uint32_t)(row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2u;
+        pl.v[kb] = (uint32_t)(row * D + ((pc ^ swz_v<D>(row)) << 3)) * 2u;
+    }
+    return pl;
+}
+
 // Issue this wave's share (transfers first .. first + CNT - 1 of a round) of
 // the transfers of one round of KW tiles into LDS starting at `buf`. Tile j of
-// the round goes to buf + j * BUF_BYTES; K transfers first, then V. Keys
-// beyond a tile's valid range are fetched from the tile's first key instead
-// (always valid); the softmax masks them, and they are finite, so a zero
-// weight times them stays zero. A round slot past the last tile re-fetches the
-// last tile (the slot is never multiplied), which keeps every wave's transfer
-// count per round fixed for the vmcnt bookkeeping. All addresses (and the page
-// ids they need from LDS) are formed before the first transfer is issued.
+// the round goes to buf + j * BUF_BYTES; K transfers first, then V; the TPP
+// transfers of one page are consecutive and never split between waves.
+//  * Full prefix tile: one page id (read from LDS, wave-uniform) gives a
+//    scalar base; the lane part is the fixed PageLanes offset.
+//  * Tree tile, or the tile that crosses the end of the prefix: per-lane
+//    addresses. Keys beyond the valid range are fetched from a valid key
+//    instead (tree: the last node; prefix: the tile's first key); the softmax
+//    masks them, and they are finite, so a zero weight times them stays zero.
+// A round slot past the last tile re-fetches the last tile (the slot is never
+// multiplied), which keeps every wave's transfer count per round fixed for
+// the vmcnt bookkeeping.
 template <int D, int CNT, typename SrcFn>
 __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* vp, const uint16_t* kt,
                                             const uint16_t* vt, int N, int Hkv, SrcFn tile_src, int round_first_tile,
-                                            int n_tiles,
-                                            int b, int kvh, int p_begin, const int* s_pages, uint32_t buf,
-                                            int first, int lane) {
+                                            int n_tiles, int b, int kvh, const int* s_pages,
+                                            const PageLanes<D>& pl, uint32_t buf, int first, int lane) {
     using Gm = Geo<D>;
+    constexpr int TPP = PageLanes<D>::TPP;
+    static_assert(CNT % TPP == 0, "a wave moves whole pages");
+    first = __builtin_amdgcn_readfirstlane(first);       // wave index based: uniform
     const int rsub = lane / Gm::CPR, pc = lane % Gm::CPR;
-    constexpr int BATCH = CNT < 4 ? CNT : 4;
-    static_assert(CNT % BATCH == 0, "transfer count must be a multiple of the batch");
     #pragma unroll
-    for (int k0 = 0; k0 < CNT; k0 += BATCH) {
-    const uint16_t* gp[BATCH];
-    #pragma unroll
-    for (int kb = 0; kb < BATCH; ++kb) {
-        const int i = first + k0 + kb;                   // wave-uniform transfer index in the round
-        const int j = i / Gm::XFER_PER_TILE;
-        const int ii = i % Gm::XFER_PER_TILE;
-        const TileSrc src = tile_src(min(round_first_tile + j, n_tiles - 1));
-        const bool isv = ii >= Gm::KB_PER_TILE;
-        const int blk = isv ? ii - Gm::KB_PER_TILE : ii;
-        const int row = blk * Gm::ROWS_PER_KB + rsub;    // key within the tile
-        const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-        const int tb = src.t0 + blk * Gm::ROWS_PER_KB;   // first key of this transfer (uniform)
-        if (src.tree) {
-            // tree tile: node rows, clamped to the last node
-            const int t = min(src.t0 + row, src.limit - 1);
-            gp[kb] = (isv ? vt : kt) + (((long)b * N + t) * Hkv + kvh) * D + c * 8;
-        } else if (src.t0 + kKeyTile <= src.limit) {
-            // full prefix tile: the transfer's 1 KB lies in one page; page base in
-            // scalar registers, lane part = row in page and chunk
-            const int page = __builtin_amdgcn_readfirstlane(s_pages[(tb >> 4) - p_begin]);
-            const long pbase = ((long)page * Hkv + kvh) * (kPage * D) + (long)(tb & 15) * D;
-            gp[kb] = (isv ? vp : kp) + pbase + rsub * D + c * 8;
+    for (int g = 0; g < CNT / TPP; ++g) {
+        const int i0 = first + g * TPP;                  // wave-uniform transfer index in the round
+        const int j = i0 / Gm::XFER_PER_TILE;
+        const int ii0 = i0 % Gm::XFER_PER_TILE;
+        const bool isv = ii0 >= Gm::KB_PER_TILE;
+        const int pq = (isv ? ii0 - Gm::KB_PER_TILE : ii0) / TPP;   // page of the tile
+        const int it = min(round_first_tile + j, n_tiles - 1);
+        const TileSrc src = tile_src(it);
+        const uint32_t lds0 = buf + j * Gm::BUF_BYTES + ii0 * 1024;
+        if (!src.tree && src.t0 + kKeyTile <= src.limit) {
+            // prefix tiles start on page boundaries; s_pages[k] = page of the split's k-th 16 tokens
+            const int page = __builtin_amdgcn_readfirstlane(s_pages[it * (kKeyTile / kPage) + pq]);
+            const uint16_t* base = (isv ? vp : kp) + ((long)page * Hkv + kvh) * (kPage * D);
+            #pragma unroll
+            for (int kb = 0; kb < TPP; ++kb)
+                dma16_s(__builtin_amdgcn_readfirstlane(lds0 + kb * 1024), base, isv ? pl.v[kb] : pl.k[kb]);
         } else {
-            // the tile that crosses the end of the prefix: keys past it read the
-            // tile's first key instead (valid and finite; the softmax masks them)
-            int t = src.t0 + row;
-            if (t >= src.limit) t = src.t0;
-            const int page = s_pages[(t >> 4) - p_begin];
-            gp[kb] = (isv ? vp : kp) + (((long)page * Hkv + kvh) * kPage + (t & 15)) * D + c * 8;
+            #pragma unroll
+            for (int kb = 0; kb < TPP; ++kb) {
+                const int row = pq * kPage + kb * Gm::ROWS_PER_KB + rsub;     // key within the tile
+                const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+                const uint16_t* gp;
+                if (src.tree) {
+                    const int t = min(src.t0 + row, src.limit - 1);
+                    gp = (isv ? vt : kt) + (((long)b * N + t) * Hkv + kvh) * D + c * 8;
+                } else {
+                    int t = src.t0 + row;
+                    if (t >= src.limit) t = src.t0;
+                    const int page = s_pages[(t >> 4) - (src.t0 >> 4) + it * (kKeyTile / kPage)];
+                    gp = (isv ? vp : kp) + (((long)page * Hkv + kvh) * kPage + (t & 15)) * D + c * 8;
+                }
+                dma16(__builtin_amdgcn_readfirstlane(lds0 + kb * 1024), gp);
+            }
         }
-    }
-    #pragma unroll
-    for (int kb = 0; kb < BATCH; ++kb) {
-        const int i = first + k0 + kb;
-        const int j = i / Gm::XFER_PER_TILE, ii = i % Gm::XFER_PER_TILE;
-        dma16(__builtin_amdgcn_readfirstlane(buf + j * Gm::BUF_BYTES + ii * 1024), gp[kb]);
-    }
     }
 }
 
@@ -253,10 +296,13 @@ __device__ __forceinline__ void tile_product(RowState<D>& st, const char* kbuf, 
         }
     }
     // online softmax (log2 domain), lazy rescale
-    float mx = NEG;
+    float mxa = NEG, mxb = NEG;
     #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    for (int r = 0; r < 16; r += 2) {
+        mxa = max3f(mxa, sacc[0][r], sacc[1][r]);
+        mxb = max3f(mxb, sacc[0][r + 1], sacc[1][r + 1]);
+    }
+    const float mx = max_halves(fmaxf(mxa, mxb)) * scale_log2;
     // move the reference max only when some row's max grew by more than 2^8
     if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.f)) {
         const float m_new = fmaxf(st.m, mx);
@@ -335,7 +381,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     const int b = t1 / a.Hkv;
     const int item = (b * a.Hkv + kvh) * a.nrb + rb;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index: uniform
     const int rw = w % RW, kw = w / RW;
     const int hf = lane >> 5, l32 = lane & 31;
     const int rloc = rw * 32 + l32;                 // row within the row block
@@ -455,6 +502,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         v_off[dt] = key * Gm::ROW_BYTES + (((d >> 3) ^ swz_v<D>(key)) << 4) + ((d >> 2) & 1) * 8;
     }
 
+    const PageLanes<D> pl = page_lanes<D>(lane);
+
     RowState<D> st;
     #pragma unroll
     for (int i = 0; i < DT; ++i) st.o[i] = f32x16{};
@@ -471,7 +520,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         #pragma unroll
         for (int p = 0; p < RING_R - 1; ++p)
             if (p < n_rounds)
-                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, p * KW, n_tiles, b, kvh, p_begin, s_pages,
+                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, p * KW, n_tiles, b, kvh, s_pages, pl,
                                     ring0 + p * KW * Gm::BUF_BYTES, w * DPR, lane);
     }
     for (int r = 0; r < n_rounds; ++r) {
@@ -479,11 +528,11 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             wait_rounds<DPR>(min(n_rounds - 1 - r, RING_R - 2));
             __syncthreads();      // round r is in LDS for every wave; the buffers of round r-1 are free
             if (r + RING_R - 1 < n_rounds)
-                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, (r + RING_R - 1) * KW, n_tiles, b, kvh, p_begin, s_pages,
+                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, (r + RING_R - 1) * KW, n_tiles, b, kvh, s_pages, pl,
                                     ring0 + ((r + RING_R - 1) % RING_R) * KW * Gm::BUF_BYTES, w * DPR, lane);
         } else {
             __syncthreads();      // every wave is done with the previous round
-            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, p_begin, s_pages, ring0, w * DPR, lane);
+            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl, ring0, w * DPR, lane);
             wait_vm<0>();
             __syncthreads();
         }
@@ -526,12 +575,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
-                st_agent16(ro, (pr * D + dt * 32 + 8 * rq + 4 * hf) * 4, v);
+                st16(ro, (pr * D + dt * 32 + 8 * rq + 4 * hf) * 4, v);
             }
         }
         if (hf == 0) {
             const u32x2 ml = {__float_as_uint(bad ? NANF : st.m), __float_as_uint(bad ? NANF : l_tot)};
-            st_agent8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
+            st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
         }
     } else {
         // merge the KW key groups through LDS
@@ -596,10 +645,10 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rl;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         #pragma unroll
-        for (int c = 0; c < CPT; ++c) st_agent16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4, acc[c]);
+        for (int c = 0; c < CPT; ++c) st16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4, acc[c]);
         if (part == 0) {
             const u32x2 ml = {__float_as_uint(bad ? NANF : M), __float_as_uint(bad ? NANF : Ls)};
-            st_agent8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
+            st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
         }
     }
 
@@ -607,9 +656,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     wait_own_stores();
     __syncthreads();
     if (tid == 0) {
-        const int old = arrive(&a.counters[item]);
+        const int old = arrive_release(&a.counters[item]);
         s_last = (old == n_act - 1);
-        if (s_last) reset_counter(&a.counters[item]);
+        if (s_last) {
+            reset_counter(&a.counters[item]);
+            acquire_agent();
+        }
     }
     __syncthreads();
     if (!s_last) return;
@@ -637,8 +689,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             for (int j = 0; j < SB; ++j) {
                 const uint32_t pr = base + (uint32_t)min(sp0 + j, n_act - 1) * RB;
                 #pragma unroll
-                for (int c = 0; c < CPT; ++c) v[j][c] = ld_agent16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4);
-                ml[j] = ld_agent8(rml, pr * 8);
+                for (int c = 0; c < CPT; ++c) v[j][c] = ld16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4);
+                ml[j] = ld8(rml, pr * 8);
             }
             float mb = NEG;
             #pragma unroll
@@ -693,10 +745,17 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     AttnPlanBf16 p{};
     const long rows = (long)(s.Hq / s.Hkv) * s.N;
     // few rows -> key groups keep several tiles in flight per workgroup
-    if (rows <= 32) { p.rw = 1; p.kw = 4; }
-    else if (rows <= 64) { p.rw = 2; p.kw = 2; }
+    if (rows <= 64) { p.rw = 1; p.kw = 4; }
     else if (rows <= 128) { p.rw = 4; p.kw = 2; }
     else { p.rw = 8; p.kw = 1; }
+    // tuning override: JF_RW = 1, 2, 4 or 8 row groups (key groups follow)
+    switch (env_int("JF_RW", 0)) {
+        case 1: p.rw = 1; p.kw = 4; break;
+        case 2: p.rw = 2; p.kw = 2; break;
+        case 4: p.rw = 4; p.kw = 2; break;
+        case 8: p.rw = 8; p.kw = 1; break;
+        default: break;
+    }
     p.rb = 32 * p.rw;
     p.nrb = (int)((rows + p.rb - 1) / p.rb);
     p.items = s.B * s.Hkv * p.nrb;

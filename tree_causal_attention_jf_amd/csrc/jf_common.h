@@ -40,46 +40,55 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
 
 // Cross-workgroup hand-off (split merge, argmax merge, acceptance walk).
 //
-// MI355X has one L2 per XCD and they are not coherent with each other. A
-// result that a workgroup on another XCD will read is therefore written and
-// read with agent-scope accesses (cache policy sc1): such a store is complete
-// only once it is visible device-wide, and such a load does not hit a stale
-// line of the local L2. No cache-wide write-back or invalidate is needed:
-//   writer: agent-scope stores, wait_own_stores() in every wave, barrier,
-//           then ONE thread bumps the agent-scope counter (arrive);
-//   reader: the thread that saw the last arrival tells the workgroup through
-//           LDS and a barrier; the workgroup reads with agent-scope loads.
+// MI355X has one L2 per XCD and they are not coherent with each other, so a
+// result read by a workgroup on another XCD has to be pushed past the writer's
+// L2 and must not be served from a stale line of the reader's.
+//
+// Bulk results (attention partials, tens of KB per workgroup) use plain
+// stores and loads around one release / acquire pair:
+//   writer: stores, wait_own_stores() in every wave, barrier, then ONE thread
+//           calls arrive_release() (agent-scope release: this XCD's L2 is
+//           written back before the counter moves);
+//   reader: the thread that saw the last arrival calls acquire_agent()
+//           (invalidates this CU's L1 and this XCD's L2), tells the workgroup
+//           through LDS and a barrier, and the workgroup then loads normally.
+// Small results (8-byte argmax keys) are written and read with agent-scope
+// atomics, which bypass the non-coherent caches, and counted with arrive().
 __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ int arrive(int* counter) {
     return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ int arrive_release(int* counter) {
+    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 __device__ __forceinline__ void reset_counter(int* counter) {
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-constexpr int kAgentScope = 16;   // buffer-instruction cache policy: sc1 (device scope)
 
 // Raw buffer over `bytes` bytes at `base` (out-of-range accesses read 0 and drop writes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void st_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAgentScope);
+__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 ld_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAgentScope));
+__device__ __forceinline__ f32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-__device__ __forceinline__ void st_agent8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kAgentScope);
+__device__ __forceinline__ void st8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
 
-__device__ __forceinline__ u32x2 ld_agent8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAgentScope);
+__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
 }  // namespace jf
