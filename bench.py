@@ -117,11 +117,11 @@ def summarize_pmc(fetch_dir, write_dir, config):
     f_fac, w_fac = copy_kib / cf, copy_kib / cw
     lines = [f"# HBM traffic of the tree attention kernel, workload {config}",
              "# made by:",
-             f"#   rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
+             f"#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
              f"python bench.py --config {config} --profile-steps 20",
-             f"#   rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv -- "
+             f"#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR -o run --output-format csv -- "
              f"python bench.py --config {config} --profile-steps 20",
-             f"#   python bench.py --config {config} --summarize-pmc {fetch_dir} {write_dir}",
+             f"#   python bench.py --config {config} --summarize-pmc FETCH_DIR WRITE_DIR",
              f"# calibration: a {COPY_BYTES >> 20} MiB copy reads FETCH_SIZE {cf:.0f} KiB and "
              f"WRITE_SIZE {cw:.0f} KiB per dispatch",
              f"#   ({cf_name[:60]}); scale factors fetch {f_fac:.4f}, write {w_fac:.4f}",
@@ -436,8 +436,9 @@ def main():
                 f()
         torch.cuda.synchronize()
         nb4, fl4 = attention_work(wl4, b4.depth.cpu().numpy())
-        t4 = time_graph(a4, 20, stream)
-        tacc4 = time_graph(acc4, 50, stream)
+        time_graph(a4, 50, stream)                     # settle the clock under sustained load
+        t4 = time_graph(a4, 300, stream)
+        tacc4 = time_graph(acc4, 1000, stream)
         tf4 = fl4 / (t4 * 1e-3) / 1e12
         lb = wl4.logits.numel() * wl4.logits.element_size()
         result["long_context"] = {
