@@ -5,12 +5,12 @@ Bars
     bonus tokens: bit-exact;
   * attention, fp32 inputs: max |out - ref| <= 1e-5 (and lse);
   * attention, bf16 inputs (fp32 accumulation): max |out - ref| <= 1e-2 and,
-    (log-sum-exp within 2^-8: the row sums add bf16-rounded weights)
     because 1/sqrt(128)-scaled data gives |out| ~ 1e-2, also
     max |out - ref| <= 1e-2 * max |ref|, plus unscaled N(0,1) variants held to
     the absolute bar. The GPU rounds P to bf16 for the P.V product and rounds
-    the output to bf16: each contributes at most 2^-9 relative, well inside
-    1e-2.
+    the output to bf16: each contributes at most 2^-8 relative, well inside
+    1e-2. The row sums add the same bf16-rounded weights, so log-sum-exp is
+    held to 2^-8 (+1e-4 for fp32 summation).
 """
 
 import itertools
