@@ -60,6 +60,12 @@ enum { JF_F32 = 0, JF_BF16 = 1 };
 /* Longest tree the 256-bit ancestor bitset can describe. */
 #define JF_MAX_NODES 256
 #define JF_PAGE_SIZE 16
+/* Most sequences one jf_tree_attention call takes (its work schedule is
+ * formed on the device from all B prefix lengths). */
+#define JF_MAX_BATCH 1024
+/* Size of the counter region at the start of every workspace (see the
+ * workspace notes of jf_tree_attention and jf_tree_accept). */
+#define JF_WORKSPACE_COUNTER_BYTES 4096
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* jf_status_string(jf_status s);
@@ -89,7 +95,7 @@ jf_status jf_build_ancestor_mask(const int32_t* parent, int32_t B, int32_t N,
 
 /* Shape of one tree-attention call. */
 typedef struct {
-    int32_t B;                 /* sequences                                        */
+    int32_t B;                 /* sequences, 0..JF_MAX_BATCH                        */
     int32_t N;                 /* tree nodes per sequence, 1..256                  */
     int32_t Hq;                /* query heads                                      */
     int32_t Hkv;               /* KV heads; Hq % Hkv == 0; head h reads KV head h / (Hq/Hkv) */
@@ -102,11 +108,17 @@ typedef struct {
 } jf_attn_shape;
 
 /*
- * Bytes of workspace jf_tree_attention needs for this shape and prefix bound.
- * Returns 0 for an invalid shape. The workspace must be zero-filled once
- * before its first use (e.g. allocated with a zeroing allocator); every call
- * leaves its counter region zero again, so it can be reused without
- * clearing. The first 256 bytes of any size are part of the counter region.
+ * Bytes of workspace jf_tree_attention needs for this shape and prefix bound
+ * (0 when the call needs none: fp32, a grid without split prefixes, or an
+ * invalid shape).
+ *
+ * Workspace contract (both jf_tree_attention and jf_tree_accept): the first
+ * JF_WORKSPACE_COUNTER_BYTES bytes are arrival counters. They must be zero
+ * before the first call (e.g. allocate with a zeroing allocator) and every
+ * call leaves them zero again; the rest is scratch that a call writes before
+ * it reads. So one workspace, sized for the largest call, can be reused by
+ * calls of any shape and by both entry points without clearing, provided the
+ * calls do not run at the same time (calls on one stream never do).
  */
 size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_prefix_len);
 
@@ -138,9 +150,10 @@ size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_pre
  * [0, max_prefix_len] or a page id it needs is outside [0, num_pages), every
  * output row of sequence b (and its lse) is set to NaN.
  *
- * Host errors: JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_DTYPE, JF_ERR_UNSUPPORTED
- * (D not 64/128, page_size not 16), JF_ERR_ALIGN (q, pages, tree K/V, out or
- * workspace not 16-byte aligned), JF_ERR_WORKSPACE, JF_ERR_LAUNCH.
+ * Host errors: JF_ERR_NULL, JF_ERR_SHAPE (including B > JF_MAX_BATCH),
+ * JF_ERR_DTYPE, JF_ERR_UNSUPPORTED (D not 64/128, page_size not 16),
+ * JF_ERR_ALIGN (q, pages, tree K/V, out or workspace not 16-byte aligned),
+ * JF_ERR_WORKSPACE, JF_ERR_LAUNCH.
  */
 jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len,
                             const void* q, const void* k_pages, const void* v_pages,
@@ -150,9 +163,9 @@ jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of workspace jf_tree_accept needs in logits mode (0 in ids mode is
- * fine: pass target_logits = NULL). Same zero-fill rule as the attention
- * workspace.
+ * Bytes of workspace jf_tree_accept needs in logits mode (ids mode needs
+ * none). Same workspace contract as jf_tree_attention: the two entry points
+ * may share one workspace.
  */
 size_t jf_tree_accept_workspace_bytes(int32_t B, int32_t N, int32_t vocab);
 
@@ -180,8 +193,8 @@ size_t jf_tree_accept_workspace_bytes(int32_t B, int32_t N, int32_t vocab);
  * array is not a valid tree are unspecified (memory-safe).
  *
  * Host errors: JF_ERR_NULL, JF_ERR_SHAPE (B < 0, N outside 1..256,
- * vocab < 1, both or neither of logits/ids), JF_ERR_DTYPE, JF_ERR_WORKSPACE
- * (logits mode), JF_ERR_LAUNCH.
+ * vocab < 1, both or neither of logits/ids, B > JF_MAX_BATCH in logits
+ * mode), JF_ERR_DTYPE, JF_ERR_WORKSPACE (logits mode), JF_ERR_LAUNCH.
  */
 jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
                          const void* target_logits, int32_t logits_dtype,

@@ -47,6 +47,14 @@ def test_every_declared_symbol_is_exported(binding):
     assert set(binding.EXPORTED) == set(_declared())
 
 
+def test_header_limits_match_the_binding(binding):
+    text = open(HEADER).read()
+    for name, value in (("JF_MAX_NODES", binding.MAX_NODES), ("JF_PAGE_SIZE", binding.PAGE_SIZE),
+                        ("JF_MAX_BATCH", binding.JF_MAX_BATCH),
+                        ("JF_WORKSPACE_COUNTER_BYTES", binding.JF_WORKSPACE_COUNTER_BYTES)):
+        assert re.search(r"#define %s (\d+)" % name, text).group(1) == str(value), name
+
+
 def test_status_strings_and_version(binding):
     for code in range(8):
         assert binding.status_string(code)
@@ -102,11 +110,16 @@ def test_workspace_queries(binding):
     # fp32 never needs scratch; an invalid shape reports 0
     assert binding.tree_attention_workspace_bytes(_shape(binding, dtype=binding.JF_F32), 2048) == 0
     assert binding.tree_attention_workspace_bytes(_shape(binding, D=96), 2048) == 0
-    # a single split needs none either
+    # a grid without split prefixes needs none
     assert binding.tree_attention_workspace_bytes(_shape(binding), 0) == 0
-    a = binding.tree_attention_workspace_bytes(_shape(binding, B=8, N=256, num_pages=2048, max_pages_per_seq=256), 4096)
-    b = binding.tree_attention_workspace_bytes(_shape(binding, B=8, N=256, num_pages=2048, max_pages_per_seq=256), 1024)
-    assert a >= b >= 0
+    # split prefixes: the fixed counter region, then the partials
+    a = binding.tree_attention_workspace_bytes(_shape(binding), 2048)
+    assert a > binding.JF_WORKSPACE_COUNTER_BYTES
+    c = binding.tree_attention_workspace_bytes(_shape(binding, B=4, N=256, num_pages=8192,
+                                                      max_pages_per_seq=2048), 32768)
+    assert c > binding.JF_WORKSPACE_COUNTER_BYTES
+    # more sequences than one call takes
+    assert binding.tree_attention_workspace_bytes(_shape(binding, B=binding.JF_MAX_BATCH + 1), 2048) == 0
     assert binding.tree_accept_workspace_bytes(4, 256, 151936) > 4 * 256 * 4
     assert binding.tree_accept_workspace_bytes(0, 0, 10) == 0
 
@@ -139,3 +152,6 @@ def test_mask_and_accept_host_checks(binding):
     for n in ("draft", "parent", "anc", "next", "alen", "nodes", "bonus"):
         assert acc(nul=(n,)) == JF_ERR_NULL, n
     assert acc(B=0, ws=ctypes.c_void_p(16), wsb=need) == JF_OK   # empty batch: no launch
+    # logits mode keeps one arrival counter per sequence in the fixed counter region
+    big = binding.tree_accept_workspace_bytes(binding.JF_MAX_BATCH + 1, 8, 1000)
+    assert acc(B=binding.JF_MAX_BATCH + 1, ws=ctypes.c_void_p(16), wsb=big) == JF_ERR_SHAPE

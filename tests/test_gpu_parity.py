@@ -244,6 +244,60 @@ def test_attention_bf16_small(jf, case, unscaled):
     check_bf16(out, ref, lse, lref, f"{name}{' unscaled' if unscaled else ''}", abs_tol=derived_bf16_bar(wl))
 
 
+@pytest.mark.parametrize("rw,splits", [(1, 1), (1, 7), (2, 3), (4, 5), (8, 2), (8, 64), (4, 0)])
+def test_attention_bf16_forced_plans(jf, rw, splits, monkeypatch):
+    # every row-group layout, with the prefix cut into several splits merged by the
+    # last one to finish (including more splits than some sequences have tiles)
+    monkeypatch.setenv("JF_RW", str(rw))
+    monkeypatch.setenv("JF_SPLITS", str(splits))
+    for D, Hq, Hkv in ((128, 8, 2), (64, 16, 2)):
+        wl = W.make_workload("c1_chain16", 5, with_accept=False, B=4, N=150, prefix=("list", [700, 0, 1, 2100]),
+                             Hq=Hq, Hkv=Hkv, D=D, tree=("random", 9))
+        out, lse = run_attention(jf, wl, to_dev(wl))
+        ref, lref = _oracle_full(wl)
+        check_bf16(out, ref, lse, lref, f"rw {rw} splits {splits} D {D}", abs_tol=derived_bf16_bar(wl))
+
+
+def test_one_workspace_serves_every_shape(jf, monkeypatch):
+    # one workspace, used in turn by attention calls whose partial layouts differ
+    # and by logits-mode acceptance: each call must find the counter region zero
+    # and leave it zero, whatever the previous call wrote past it
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=DEV)
+    cases = [
+        (7, dict(B=4, N=150, prefix=("list", [700, 0, 1, 2100]), Hq=8, Hkv=2, D=128, tree=("random", 9))),
+        (0, dict(B=8, N=256, prefix=("list", [900, 1500, 64, 3000, 17, 1200, 800, 2500]), Hq=8, Hkv=2, D=128,
+                 tree=("best_first", 4, 12, 2.0))),
+        (3, dict(B=3, N=40, prefix=("list", [100, 333, 1]), Hq=16, Hkv=2, D=64, tree=("random", 7))),
+    ]
+    for rnd in range(2):
+        for splits, kw in cases:
+            if splits:
+                monkeypatch.setenv("JF_SPLITS", str(splits))
+            else:
+                monkeypatch.delenv("JF_SPLITS", raising=False)
+            wl = W.make_workload("c1_chain16", 7 + rnd, with_accept=False, **kw)
+            out, lse = run_attention(jf, wl, to_dev(wl), workspace=ws)
+            rows = _sampled_rows(wl, 40, rnd)
+            ref, lref = _oracle_full(wl, rows=rows)
+            idx = tuple(np.array(rows).T)
+            check_bf16(torch.from_numpy(out.float().cpu().numpy()[idx]), ref[idx], lse.cpu()[idx], lref[idx],
+                       f"shared workspace round {rnd} splits {splits}", abs_tol=derived_bf16_bar(wl))
+            # acceptance over logits with the same workspace, between the attention calls
+            acc = W.make_workload("c1_chain16", 30 + rnd, prefix=("fixed", 16), B=5, N=24,
+                                  tree=("random", 6), accept=("logits", 5000, 3.0, 0.8))
+            P = acc.parent.to(DEV)
+            anc, _, _ = jf.build_ancestor_mask(P)
+            alen, nodes, bonus, nxt = jf.tree_accept(P, anc, acc.draft.to(DEV), logits=acc.logits.to(DEV),
+                                                     workspace=ws)
+            torch.cuda.synchronize()
+            nref = oracle.target_choice(acc.logits)
+            ra, rn, rb = oracle.tree_accept(acc.parent.numpy(), acc.draft.numpy(), nref)
+            assert np.array_equal(nxt.cpu().numpy(), nref)
+            assert np.array_equal(alen.cpu().numpy(), ra) and np.array_equal(nodes.cpu().numpy(), rn)
+            assert np.array_equal(bonus.cpu().numpy(), rb)
+    assert not ws[:4096].any(), "counter region left non-zero"
+
+
 def test_attention_bf16_c1_full(jf):
     for seed in (0, 1):
         for unscaled in (False, True):

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libjf_tree.so")
 JF_F32, JF_BF16 = 0, 1
 MAX_NODES = 256
 PAGE_SIZE = 16
+JF_MAX_BATCH = 1024          # sequences per tree_attention call (include/jf_tree.h)
+JF_WORKSPACE_COUNTER_BYTES = 4096   # counter region at the start of every workspace
 
 EXPORTED = (
     "jf_status_string",
@@ -119,9 +121,10 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 class Workspace:
     """Zero-initialised scratch buffers, one per (device, purpose). The
-    library leaves its counter region zero after every call, so a buffer is
-    cleared only when it is first allocated or grown. Not for calls that are
-    in flight concurrently on different streams."""
+    library leaves the fixed counter region at the start of a workspace zero
+    after every call and writes the rest before reading it, so a buffer is
+    cleared only when it is first allocated or grown, and serves calls of any
+    shape. Not for calls that are in flight concurrently on different streams."""
 
     def __init__(self):
         self._bufs = {}

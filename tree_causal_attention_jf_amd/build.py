@@ -6,6 +6,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -33,6 +34,12 @@ def _hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+# Kernels whose loops count their own vector-memory operations (s_waitcnt vmcnt
+# with hand-computed limits): a register spill would add scratch loads to that
+# count and let a wait return early, so such a kernel must use no scratch.
+NO_SCRATCH_KERNELS = ("tree_attn_bf16_kernel",)
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,6 +50,21 @@ def _run(cmd, verbose):
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out)
+    return out
+
+
+def check_no_scratch(remarks: str) -> None:
+    """Raise if a kernel in NO_SCRATCH_KERNELS reports scratch (from the compiler's
+    kernel-resource-usage remarks)."""
+    fn = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and fn and any(k in fn for k in NO_SCRATCH_KERNELS) and int(m.group(1)) > 0:
+            raise RuntimeError(f"{fn} uses {m.group(1)} bytes of scratch per lane (register spills)")
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -54,9 +76,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = ["-Rpass-analysis=kernel-resource-usage"] if src == "attn_bf16.hip" else []
+        cmds.append([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
-        list(ex.map(lambda c: _run(c, verbose), cmds))
+        outs = list(ex.map(lambda c: _run(c, verbose and "-Rpass-analysis" not in " ".join(c)), cmds))
+    for out in outs:
+        check_no_scratch(out)
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)

@@ -348,8 +348,8 @@ AcceptPlan plan_accept(int B, int N, int vocab) {
     chunks = (vocab + len - 1) / len;
     p.chunks = chunks;
     p.chunk_len = len;
-    p.off_seq = 0;
-    p.off_part = align_up((size_t)B * 4, 256);
+    p.off_seq = 0;                                     // B <= kMaxCounters (host check)
+    p.off_part = kCounterBytes;
     p.bytes = p.off_part + align_up((size_t)rows * chunks * 8, 256);
     return p;
 }

@@ -31,7 +31,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 jf_status check_attn_shape(const jf_attn_shape* s, int32_t max_prefix_len) {
     if (!s) return JF_ERR_NULL;
     if (s->dtype != JF_F32 && s->dtype != JF_BF16) return JF_ERR_DTYPE;
-    if (s->B < 0 || s->N < 1 || s->N > JF_MAX_NODES || s->Hq < 1 || s->Hkv < 1 || s->Hq % s->Hkv != 0)
+    if (s->B < 0 || s->B > JF_MAX_BATCH || s->N < 1 || s->N > JF_MAX_NODES || s->Hq < 1 || s->Hkv < 1 ||
+        s->Hq % s->Hkv != 0)
         return JF_ERR_SHAPE;
     if (s->num_pages < 0 || s->max_pages_per_seq < 0) return JF_ERR_SHAPE;
     if (s->D != 64 && s->D != 128) return JF_ERR_UNSUPPORTED;
@@ -42,6 +43,8 @@ jf_status check_attn_shape(const jf_attn_shape* s, int32_t max_prefix_len) {
     // index arithmetic inside the kernels: grid and row counts fit 32 bits
     const long rows = (long)(s->Hq / s->Hkv) * s->N;
     if ((long)s->B * s->Hkv * ((rows + 63) / 64) * ((max_prefix_len / 64) + 1) > 0x7fffffffL) return JF_ERR_SHAPE;
+    // work units (64-key tiles per sequence and KV head) counted in 32 bits per sequence
+    if ((long)s->B * ((max_prefix_len + 63) / 64 + (s->N + 63) / 64) > 0x7fffffffL / s->Hkv) return JF_ERR_SHAPE;
     return JF_OK;
 }
 
@@ -126,6 +129,7 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target
         if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
         if (!aligned16(workspace)) return JF_ERR_ALIGN;
         if ((long)B * N * ((vocab + 4095) / 4096) > 0x7fffffffL) return JF_ERR_SHAPE;
+        if (B > JF_WORKSPACE_COUNTER_BYTES / 4) return JF_ERR_SHAPE;   // one counter per sequence
     }
     if (B == 0) return JF_OK;
     const hipError_t e = jf::launch_accept(B, N, vocab, target_logits, logits_dtype, target_ids, draft_tokens,

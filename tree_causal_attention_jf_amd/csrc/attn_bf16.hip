@@ -49,6 +49,7 @@ constexpr int kKeyTile = 64;
 constexpr int kRing = 4;                 // LDS tile buffers
 constexpr int kMaxPagesPerSplit = 1024;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxOrdered = 64;          // batches ranked by prefix length inside the kernel
 
 struct AttnArgs {
     const uint16_t* q;
@@ -70,6 +71,7 @@ struct AttnArgs {
     int nrb;           // row blocks per (sequence, KV head)
     int splits;        // splits per row block in the grid
     int pps;           // prefix pages per split (multiple of 4)
+    int order;         // 1: walk the sequences longest first (B <= kMaxOrdered)
     float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -306,7 +308,9 @@ __device__ __forceinline__ void tile_product(RowState<D>& st, const char* kbuf, 
     // move the reference max only when some row's max grew by more than 2^8
     if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.f)) {
         const float m_new = fmaxf(st.m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);   // m = -inf -> 0
+        // a row with no visible key yet keeps m = -inf (its l and O are 0): rescaling
+        // against 0 instead of -inf gives alpha = 0, not exp2(-inf + inf) = NaN
+        const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == NEG ? 0.f : m_new));
         st.l *= alpha;
         #pragma unroll
         for (int i = 0; i < DT; ++i) st.o[i] *= alpha;
@@ -370,19 +374,37 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     __shared__ float s_ml[KW][RB][2];
     __shared__ unsigned long long s_union[kAncWords];
     __shared__ int s_last;
+    __shared__ int s_seq;
 
-    // ---- which (sequence, KV head, split, row block) this workgroup owns
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index: uniform
+
+    // ---- which (sequence, KV head, split, row block) this workgroup owns. Workgroups
+    // start in id order as CUs free up; with `order`, the ids walk the sequences from
+    // the longest prefix to the shortest, so short work fills in at the end.
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int rb = lid % a.nrb;
     int t1 = lid / a.nrb;
     const int s = t1 % a.splits;
     t1 /= a.splits;
     const int kvh = t1 % a.Hkv;
-    const int b = t1 / a.Hkv;
+    int b = t1 / a.Hkv;
+    if (a.order) {
+        if (w == 0) {
+            // rank of sequence `lane` = number of sequences before it (longer, or as
+            // long with a smaller index); the sequence of rank b is ours
+            const int Lm = lane < a.B ? a.prefix_len[lane] : -1;
+            int rank = 0;
+            for (int j = 0; j < a.B; ++j) {
+                const int Lj = __shfl(Lm, j);
+                rank += (Lj > Lm || (Lj == Lm && j < lane)) ? 1 : 0;
+            }
+            if (lane < a.B && rank == b) s_seq = lane;
+        }
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(s_seq);
+    }
     const int item = (b * a.Hkv + kvh) * a.nrb + rb;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index: uniform
     const int rw = w % RW, kw = w / RW;
     const int hf = lane >> 5, l32 = lane & 31;
     const int rloc = rw * 32 + l32;                 // row within the row block
@@ -728,10 +750,17 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
-    int rw, kw, rb, nrb, items, splits, pps;
+    int rw, kw, rb, nrb, items, splits, pps, order;
     long grid;
-    size_t off_cnt, off_ml, off_o, bytes;
+    size_t off_cnt, fill_bytes, off_ml, off_o, bytes;
 };
+
+// Zero the counters past the fixed region (a kernel, so that the call can be
+// captured in a graph).
+__global__ void zero_words(int* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -747,7 +776,7 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     // few rows -> key groups keep several tiles in flight per workgroup
     if (rows <= 64) { p.rw = 1; p.kw = 4; }
     else if (rows <= 128) { p.rw = 4; p.kw = 2; }
-    else { p.rw = 8; p.kw = 1; }
+    else { p.rw = 8; p.kw = 1; }   // (128-row blocks hold one prefetch round: slower)
     // tuning override: JF_RW = 1, 2, 4 or 8 row groups (key groups follow)
     switch (env_int("JF_RW", 0)) {
         case 1: p.rw = 1; p.kw = 4; break;
@@ -777,6 +806,7 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     p.splits = splits;
     p.pps = pps;
     p.grid = (long)p.items * splits;
+    p.order = (s.B > 1 && s.B <= kMaxOrdered && p.grid > 256) ? 1 : 0;
     // split partials are addressed with 32-bit buffer offsets
     while (splits > 1 && (size_t)p.items * splits * p.rb * s.D * 4 >= (size_t)0xffffff00u) {
         splits = (splits + 1) / 2;
@@ -789,8 +819,11 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
         p.grid = (long)p.items * splits;
     }
     if (splits > 1) {
+        // counters: the fixed region of every workspace (self-cleaning), extended past
+        // it, and zero-filled before the launch, only for more than kMaxCounters items
         p.off_cnt = 0;
-        p.off_ml = align256((size_t)p.items * 4);
+        p.fill_bytes = p.items > kMaxCounters ? align256((size_t)(p.items - kMaxCounters) * 4) : 0;
+        p.off_ml = kCounterBytes + p.fill_bytes;
         p.off_o = p.off_ml + align256((size_t)p.items * splits * p.rb * 2 * 4);
         p.bytes = p.off_o + align256((size_t)p.items * splits * p.rb * s.D * 4);
     }
@@ -846,6 +879,12 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.nrb = p.nrb;
     a.splits = p.splits;
     a.pps = p.pps;
+    a.order = p.order;
+    if (p.splits > 1 && p.fill_bytes > 0) {
+        const int n = (int)(p.fill_bytes / 4);
+        hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream,
+                           reinterpret_cast<int*>(ws + kCounterBytes), n);
+    }
     a.scale_log2 = s.sm_scale * 1.44269504088896340736f;
     return s.D == 128 ? launch_bf16_d<128>(p, a, stream) : launch_bf16_d<64>(p, a, stream);
 }

@@ -20,6 +20,13 @@ constexpr int kAncWords = 4;
 constexpr int kPage = JF_PAGE_SIZE;
 constexpr int kNumXcd = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// Every workspace starts with a counter region of this fixed size, whatever the
+// shape of the call: counters are zero before and after every call, and
+// everything past them is scratch each call writes before it reads. So one
+// workspace can serve calls of any shape, one at a time.
+constexpr int kCounterBytes = JF_WORKSPACE_COUNTER_BYTES;
+constexpr int kMaxCounters = kCounterBytes / 4;
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
