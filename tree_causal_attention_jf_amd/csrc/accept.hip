@@ -178,36 +178,63 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_ids_kernel(
 template <typename T>
 __device__ __forceinline__ void scan_chunk(const T* __restrict__ row, int lo, int hi, Best& b);
 
-// bf16: 8 values per 16-byte load; the row start must be 16-byte aligned
+// bf16: 8 values per 16-byte load; the row start must be 16-byte aligned.
+// A thread visits its indices in increasing order, so a strictly larger value is
+// the only thing that can replace its best (an equal one comes later and loses).
+// Per 8 values: the max of the vector (v_max3 ignores NaN), and only when it beats
+// the best so far, the first position holding it. A thread that has recorded
+// nothing yet also takes a vector whose max equals its -inf start, so a row of
+// -inf values still yields its first index.
+__device__ __forceinline__ void offer8_bf16(const u32x4 r, int i0, Best& b) {
+    float v[8];
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(r[e] << 16);
+        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+    }
+    const float m = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), max3f(v[6], v[7], v[7]));
+    if (m != m) {
+        // all NaN, or a signalling NaN among them: value by value
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) offer(b, v[e], i0 + e);
+    } else if (m > b.v || (b.i == kNoIndex)) {
+        int k = 7;
+        #pragma unroll
+        for (int e = 6; e >= 0; --e) k = (v[e] == m) ? e : k;
+        b.v = m;
+        b.i = i0 + k;
+    }
+}
+
 template <>
 __device__ __forceinline__ void scan_chunk<uint16_t>(const uint16_t* __restrict__ row, int lo, int hi, Best& b) {
     const int nvec = (hi - lo) >> 3;
     const u32x4* vp = reinterpret_cast<const u32x4*>(row + lo);
     constexpr int U = 4;
+    constexpr int STEP = U * kAcceptThreads;
     int k = threadIdx.x;
-    for (; k + (U - 1) * kAcceptThreads < nvec; k += U * kAcceptThreads) {
-        u32x4 r[U];
+    // two batches in flight: the next batch is requested before the current one is scanned
+    u32x4 cur[U];
+    const bool any = k + (U - 1) * kAcceptThreads < nvec;
+    if (any) {
         #pragma unroll
-        for (int j = 0; j < U; ++j) r[j] = __builtin_nontemporal_load(vp + k + j * kAcceptThreads);
-        #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int i0 = lo + ((k + j * kAcceptThreads) << 3);
+        for (int j = 0; j < U; ++j) cur[j] = __builtin_nontemporal_load(vp + k + j * kAcceptThreads);
+    }
+    for (; k + (U - 1) * kAcceptThreads < nvec; k += STEP) {
+        u32x4 nxt[U];
+        const bool more = k + STEP + (U - 1) * kAcceptThreads < nvec;
+        if (more) {
             #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                offer(b, bf16_bits_to_f32(r[j][e] & 0xffffu), i0 + 2 * e);
-                offer(b, bf16_bits_to_f32(r[j][e] >> 16), i0 + 2 * e + 1);
-            }
+            for (int j = 0; j < U; ++j) nxt[j] = __builtin_nontemporal_load(vp + k + STEP + j * kAcceptThreads);
         }
-    }
-    for (; k < nvec; k += kAcceptThreads) {
-        const u32x4 r = __builtin_nontemporal_load(vp + k);
-        const int i0 = lo + (k << 3);
         #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            offer(b, bf16_bits_to_f32(r[e] & 0xffffu), i0 + 2 * e);
-            offer(b, bf16_bits_to_f32(r[e] >> 16), i0 + 2 * e + 1);
+        for (int j = 0; j < U; ++j) offer8_bf16(cur[j], lo + ((k + j * kAcceptThreads) << 3), b);
+        if (more) {
+            #pragma unroll
+            for (int j = 0; j < U; ++j) cur[j] = nxt[j];
         }
     }
+    for (; k < nvec; k += kAcceptThreads) offer8_bf16(__builtin_nontemporal_load(vp + k), lo + (k << 3), b);
     for (int i = lo + (nvec << 3) + threadIdx.x; i < hi; i += kAcceptThreads)
         offer(b, bf16_bits_to_f32(row[i]), i);
 }
@@ -338,7 +365,7 @@ AcceptPlan plan_accept(int B, int N, int vocab) {
     AcceptPlan p{};
     const long rows = (long)B * N;
     const int min_chunk = 8192;                        // >= 32 values (4 loads) per thread
-    int chunks = (int)((1024 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~1024 workgroups
+    int chunks = (int)((2048 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~2048 workgroups
     const int max_chunks = (vocab + min_chunk - 1) / min_chunk;
     chunks = chunks < 1 ? 1 : chunks;
     chunks = chunks > max_chunks ? max_chunks : chunks;

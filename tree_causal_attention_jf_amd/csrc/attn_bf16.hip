@@ -72,6 +72,7 @@ struct AttnArgs {
     int splits;        // splits per row block in the grid
     int pps;           // prefix pages per split (multiple of 4)
     int order;         // 1: walk the sequences longest first (B <= kMaxOrdered)
+    int tree_split;    // 1: split splits-1 runs the tree tiles alone, the others the prefix
     float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -118,13 +119,6 @@ __device__ __forceinline__ void dma16_s(uint32_t lds_base, const void* sbase, ui
                  : "memory", "m0");
 }
 
-// max(a, b, c) in one instruction (inputs are finite or -inf here, so no NaN
-// quieting is needed)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
 
 // max of a value over lanes i and i ^ 32 (swap of the two half-waves)
 __device__ __forceinline__ float max_halves(float x) {
@@ -417,8 +411,10 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     // this split's block-table entries (the page range does not depend on the
     // length), the wave's Q rows and the rows' ancestor words
     constexpr int PPT = (kMaxPagesPerSplit + T - 1) / T;
-    const int p_begin = s * a.pps;
-    const int p_avail = min(a.pps, a.max_pages - p_begin);
+    // with tree_split, the last split slot holds no prefix pages
+    const bool tree_wg = a.tree_split && s == a.splits - 1;
+    const int p_begin = tree_wg ? 0 : s * a.pps;
+    const int p_avail = tree_wg ? 0 : min(a.pps, a.max_pages - p_begin);
     int L = a.prefix_len[b];
     int pid[PPT];
     #pragma unroll
@@ -444,13 +440,23 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     bool bad = (L < 0 || L > a.max_prefix);
     if (bad) L = 0;
     const int npages = (L + kPage - 1) / kPage;
-    int n_act = (npages + a.pps - 1) / a.pps;
-    if (n_act < 1) n_act = 1;
-    if (s >= n_act) return;                                   // uniform: the whole workgroup leaves
-    const int p_end = min(npages, p_begin + a.pps);
+    // splits that hold work: the prefix splits, and the tree either in the last of
+    // them or (tree_split) in its own slot, splits - 1
+    const int n_pre_splits = (npages + a.pps - 1) / a.pps;
+    int n_act;
+    bool has_tree;
+    if (a.tree_split) {
+        n_act = n_pre_splits + 1;
+        if (!tree_wg && s >= n_pre_splits) return;            // uniform: the whole workgroup leaves
+        has_tree = tree_wg;
+    } else {
+        n_act = n_pre_splits < 1 ? 1 : n_pre_splits;
+        if (s >= n_act) return;
+        has_tree = (s == n_act - 1);
+    }
+    const int p_end = tree_wg ? 0 : min(npages, p_begin + a.pps);
     const int tok_begin = p_begin * kPage;
-    const int tok_end = min(L, p_end * kPage);
-    const bool has_tree = (s == n_act - 1);
+    const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
     if (!has_tree) ancw = u64x4{0, 0, 0, 0};
 
     if (tid < kAncWords) s_union[tid] = 0;
@@ -709,7 +715,9 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             u32x2 ml[SB];
             #pragma unroll
             for (int j = 0; j < SB; ++j) {
-                const uint32_t pr = base + (uint32_t)min(sp0 + j, n_act - 1) * RB;
+                const int kk = min(sp0 + j, n_act - 1);
+                const int slot = (a.tree_split && kk >= n_pre_splits) ? a.splits - 1 : kk;
+                const uint32_t pr = base + (uint32_t)slot * RB;
                 #pragma unroll
                 for (int c = 0; c < CPT; ++c) v[j][c] = ld16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4);
                 ml[j] = ld8(rml, pr * 8);
@@ -750,7 +758,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
-    int rw, kw, rb, nrb, items, splits, pps, order;
+    int rw, kw, rb, nrb, items, splits, pps, order, tree_split;
     long grid;
     size_t off_cnt, fill_bytes, off_ml, off_o, bytes;
 };
@@ -806,7 +814,6 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     p.splits = splits;
     p.pps = pps;
     p.grid = (long)p.items * splits;
-    p.order = (s.B > 1 && s.B <= kMaxOrdered && p.grid > 256) ? 1 : 0;
     // split partials are addressed with 32-bit buffer offsets
     while (splits > 1 && (size_t)p.items * splits * p.rb * s.D * 4 >= (size_t)0xffffff00u) {
         splits = (splits + 1) / 2;
@@ -818,6 +825,16 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
         p.pps = pps;
         p.grid = (long)p.items * splits;
     }
+    // short splits (a few rounds each): the tree tiles get a split of their own instead
+    // of adding a round (and a full memory latency) to the last prefix split
+    if (splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 0) &&
+        (size_t)p.items * (splits + 1) * p.rb * s.D * 4 < (size_t)0xffffff00u) {
+        p.tree_split = 1;
+        splits += 1;
+        p.splits = splits;
+        p.grid = (long)p.items * splits;
+    }
+    p.order = (s.B > 1 && s.B <= kMaxOrdered && p.grid > 256) ? 1 : 0;
     if (splits > 1) {
         // counters: the fixed region of every workspace (self-cleaning), extended past
         // it, and zero-filled before the launch, only for more than kMaxCounters items
@@ -880,6 +897,7 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.splits = p.splits;
     a.pps = p.pps;
     a.order = p.order;
+    a.tree_split = p.tree_split;
     if (p.splits > 1 && p.fill_bytes > 0) {
         const int n = (int)(p.fill_bytes / 4);
         hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream,

@@ -37,6 +37,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// max(a, b, c) in one v_max3_f32, without the NaN-quieting copies the compiler
+// adds around fmaxf. A quiet NaN input is ignored; a signalling NaN makes the
+// result NaN, so callers whose inputs may hold NaN check the result.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Workgroup id -> logical id such that each XCD receives one contiguous range
 // of logical ids (hardware deals workgroup x to XCD x % 8).
 __device__ __forceinline__ int xcd_remap(int x, int total) {
