@@ -365,7 +365,7 @@ AcceptPlan plan_accept(int B, int N, int vocab) {
     AcceptPlan p{};
     const long rows = (long)B * N;
     const int min_chunk = 8192;                        // >= 32 values (4 loads) per thread
-    int chunks = (int)((2048 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~2048 workgroups
+    int chunks = (int)((1024 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~1024 workgroups
     const int max_chunks = (vocab + min_chunk - 1) / min_chunk;
     chunks = chunks < 1 ? 1 : chunks;
     chunks = chunks > max_chunks ? max_chunks : chunks;
