@@ -248,16 +248,22 @@ struct RowState {
 };
 
 // Multiply one 64-key tile into a wave's running state.
-template <int D>
-__device__ __forceinline__ void tile_product(RowState<D>& st, const char* kbuf, const char* vbuf,
-                                             const bf16x8* qreg, const TileSrc& src, u64x4 ancw,
+// Multiply one 64-key tile into the running state of a wave's RPW row blocks
+// (32 query rows each). Every K and V operand read from LDS feeds the product
+// of each row block, so RPW = 2 halves the LDS traffic per product and gives the
+// wave two independent chains to interleave.
+template <int D, int RPW>
+__device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, const char* vbuf,
+                                             const bf16x8 (*qreg)[D / 16], const TileSrc& src, const u64x4* ancw,
                                              int N, float scale_log2, const int* v_off, int hf, int l32) {
     using Gm = Geo<D>;
     constexpr int DCH = D / 16;
     constexpr int DT = D / 32;
     const float NEG = -__builtin_inff();
-    // S^T = K Q^T for two 32-key halves
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // S^T = K Q^T for two 32-key halves, per row block
+    f32x16 sacc[RPW][2];
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) sacc[blk][0] = sacc[blk][1] = f32x16{};
     #pragma unroll
     for (int c = 0; c < DCH; ++c) {
         #pragma unroll
@@ -265,81 +271,94 @@ __device__ __forceinline__ void tile_product(RowState<D>& st, const char* kbuf, 
             const int key = h2 * 32 + l32;
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + key * Gm::ROW_BYTES +
                                                                (((2 * c + hf) ^ swz_k<D>(key)) << 4));
-            sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[c], sacc[h2], 0, 0, 0);
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk)
+                sacc[blk][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[blk][c], sacc[blk][h2], 0, 0, 0);
         }
     }
-    // register r of half h2 holds key h2*32 + 8*(r/4) + 4*hf + r%4 of the tile
-    if (src.tree) {
-        const int tt = src.t0 / kKeyTile;
-        const int left = N - src.t0;
-        uint64_t mw = ancw[tt];
-        if (left < 64) mw &= (1ull << left) - 1ull;
-        mw >>= 4 * hf;
-        const uint32_t lo = (uint32_t)mw, hi = (uint32_t)(mw >> 32);
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int sh = 8 * (r >> 2) + (r & 3);
-            if (!((lo >> sh) & 1u)) sacc[0][r] = NEG;
-            if (!((hi >> sh) & 1u)) sacc[1][r] = NEG;
-        }
-    } else if (src.t0 + kKeyTile > src.limit) {
-        const int nvalid = src.limit - src.t0 - 4 * hf;
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kk = 8 * (r >> 2) + (r & 3);
-            if (kk >= nvalid) sacc[0][r] = NEG;
-            if (kk + 32 >= nvalid) sacc[1][r] = NEG;
-        }
-    }
-    // online softmax (log2 domain), lazy rescale
-    float mxa = NEG, mxb = NEG;
+    uint32_t pk[RPW][2][8];
     #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        mxa = max3f(mxa, sacc[0][r], sacc[1][r]);
-        mxb = max3f(mxb, sacc[0][r + 1], sacc[1][r + 1]);
-    }
-    const float mx = max_halves(fmaxf(mxa, mxb)) * scale_log2;
-    // move the reference max only when some row's max grew by more than 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.f)) {
-        const float m_new = fmaxf(st.m, mx);
-        // a row with no visible key yet keeps m = -inf (its l and O are 0): rescaling
-        // against 0 instead of -inf gives alpha = 0, not exp2(-inf + inf) = NaN
-        const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == NEG ? 0.f : m_new));
-        st.l *= alpha;
-        #pragma unroll
-        for (int i = 0; i < DT; ++i) st.o[i] *= alpha;
-        st.m = m_new;
-    }
-    const float m_use = (st.m == NEG) ? 0.f : st.m;
-    // the row sum adds the bf16-rounded weights that the P.V product uses, two
-    // per v_dot2_f32_bf16
-    float rs = 0.f;
-    uint32_t pk[2][8];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int blk = 0; blk < RPW; ++blk) {
+        // register r of half h2 holds key h2*32 + 8*(r/4) + 4*hf + r%4 of the tile
+        if (src.tree) {
+            const int tt = src.t0 / kKeyTile;
+            const int left = N - src.t0;
+            uint64_t mw = ancw[blk][tt];
+            if (left < 64) mw &= (1ull << left) - 1ull;
+            mw >>= 4 * hf;
+            const uint32_t lo = (uint32_t)mw, hi = (uint32_t)(mw >> 32);
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int sh = 8 * (r >> 2) + (r & 3);
+                if (!((lo >> sh) & 1u)) sacc[blk][0][r] = NEG;
+                if (!((hi >> sh) & 1u)) sacc[blk][1][r] = NEG;
+            }
+        } else if (src.t0 + kKeyTile > src.limit) {
+            const int nvalid = src.limit - src.t0 - 4 * hf;
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + (r & 3);
+                if (kk >= nvalid) sacc[blk][0][r] = NEG;
+                if (kk + 32 >= nvalid) sacc[blk][1][r] = NEG;
+            }
+        }
+        // online softmax (log2 domain), lazy rescale
+        float mxa = NEG, mxb = NEG;
         #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r], scale_log2, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h2][r + 1], scale_log2, -m_use));
-            pk[h2][r >> 1] = pack_bf16x2(p0, p1);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[h2][r >> 1]), ones, rs, false);
+            mxa = max3f(mxa, sacc[blk][0][r], sacc[blk][1][r]);
+            mxb = max3f(mxb, sacc[blk][0][r + 1], sacc[blk][1][r + 1]);
         }
+        const float mx = max_halves(fmaxf(mxa, mxb)) * scale_log2;
+        RowState<D>& sb = st[blk];
+        // move the reference max only when some row's max grew by more than 2^8
+        if (__builtin_amdgcn_ballot_w64(mx > sb.m + 8.f)) {
+            const float m_new = fmaxf(sb.m, mx);
+            // a row with no visible key yet keeps m = -inf (its l and O are 0): rescaling
+            // against 0 instead of -inf gives alpha = 0, not exp2(-inf + inf) = NaN
+            const float alpha = __builtin_amdgcn_exp2f(sb.m - (m_new == NEG ? 0.f : m_new));
+            sb.l *= alpha;
+            #pragma unroll
+            for (int i = 0; i < DT; ++i) sb.o[i] *= alpha;
+            sb.m = m_new;
+        }
+        const float m_use = (sb.m == NEG) ? 0.f : sb.m;
+        // the row sum adds the bf16-rounded weights that the P.V product uses, two
+        // per v_dot2_f32_bf16
+        float rs = 0.f;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        #pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            #pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][h2][r], scale_log2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][h2][r + 1], scale_log2, -m_use));
+                pk[blk][h2][r >> 1] = pack_bf16x2(p0, p1);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[blk][h2][r >> 1]), ones, rs, false);
+            }
+        }
+        sb.l += rs;
     }
-    st.l += rs;
     // O^T += V^T P^T, 16 keys per step (two transposing reads give the 8 keys of a lane)
     #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
         const int h2 = kc >> 1, o4 = (kc & 1) * 4;
-        const u32x4 pw = {pk[h2][o4], pk[h2][o4 + 1], pk[h2][o4 + 2], pk[h2][o4 + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        bf16x8 pb[RPW];
+        #pragma unroll
+        for (int blk = 0; blk < RPW; ++blk) {
+            const u32x4 pw = {pk[blk][h2][o4], pk[blk][h2][o4 + 1], pk[blk][h2][o4 + 2], pk[blk][h2][o4 + 3]};
+            pb[blk] = __builtin_bit_cast(bf16x8, pw);
+        }
         #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const char* vp0 = vbuf + v_off[dt] + kc * 16 * Gm::ROW_BYTES;
             const u32x2 lo2 = __builtin_bit_cast(u32x2, ds_read_tr(vp0));
             const u32x2 hi2 = __builtin_bit_cast(u32x2, ds_read_tr(vp0 + 8 * Gm::ROW_BYTES));
             const u32x4 vw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb, st.o[dt], 0, 0, 0);
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk)
+                st[blk].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb[blk],
+                                                                        st[blk].o[dt], 0, 0, 0);
         }
     }
 }
@@ -351,12 +370,13 @@ __device__ __forceinline__ int merge_off(int r, int c) {
     return r * (D * 4) + ((c ^ (r & 7)) << 4);
 }
 
-template <int D, int RW, int KW>
+template <int D, int RW, int KW, int RPW>
 __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     using Gm = Geo<D>;
     constexpr int NW = RW * KW;
     constexpr int T = NW * 64;
-    constexpr int RB = RW * 32;
+    constexpr int RB = RW * 32 * RPW;                // rows per workgroup: RW waves x RPW blocks of 32
+    static_assert(RPW == 1 || KW == 1, "several row blocks per wave only without key groups");
     constexpr int DCH = D / 16;                      // k-steps of the QK product
     constexpr int DT = D / 32;                       // 32-wide d tiles of O^T
     constexpr int RING_R = kRing / KW;               // rounds the ring holds
@@ -401,11 +421,17 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     const int item = (b * a.Hkv + kvh) * a.nrb + rb;
     const int rw = w % RW, kw = w / RW;
     const int hf = lane >> 5, l32 = lane & 31;
-    const int rloc = rw * 32 + l32;                 // row within the row block
-    const int row = rb * RB + rloc;
-    const bool row_ok = row < a.rows;
-    const int node = row_ok ? row / a.G : 0;
-    const int head = kvh * a.G + (row_ok ? row % a.G : 0);
+    // the lane's row in each of the wave's row blocks
+    int rloc[RPW], node[RPW], head[RPW];
+    bool row_ok[RPW];
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        rloc[blk] = (rw * RPW + blk) * 32 + l32;    // row within the workgroup's rows
+        const int row = rb * RB + rloc[blk];
+        row_ok[blk] = row < a.rows;
+        node[blk] = row_ok[blk] ? row / a.G : 0;
+        head[blk] = kvh * a.G + (row_ok[blk] ? row % a.G : 0);
+    }
 
     // ---- every global read of the set-up is issued at once: the prefix length,
     // this split's block-table entries (the page range does not depend on the
@@ -422,19 +448,21 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         const int i = tid + k * T;
         pid[k] = (i < p_avail) ? a.block_table[(long)b * a.max_pages + p_begin + i] : 0;
     }
-    bf16x8 qreg[DCH];
-    {
-        const uint16_t* qp = a.q + (((long)b * a.N + node) * a.Hq + head) * D + 8 * hf;
+    bf16x8 qreg[RPW][DCH];
+    u64x4 ancw[RPW];
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        const uint16_t* qp = a.q + (((long)b * a.N + node[blk]) * a.Hq + head[blk]) * D + 8 * hf;
         #pragma unroll
         for (int c = 0; c < DCH; ++c) {
-            const u32x4 v = row_ok ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
-            qreg[c] = __builtin_bit_cast(bf16x8, v);
+            const u32x4 v = row_ok[blk] ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
+            qreg[blk][c] = __builtin_bit_cast(bf16x8, v);
         }
-    }
-    u64x4 ancw = {0, 0, 0, 0};
-    if (row_ok) {
-        #pragma unroll
-        for (int k = 0; k < kAncWords; ++k) ancw[k] = a.anc[((long)b * a.N + node) * kAncWords + k];
+        ancw[blk] = u64x4{0, 0, 0, 0};
+        if (row_ok[blk]) {
+            #pragma unroll
+            for (int k = 0; k < kAncWords; ++k) ancw[blk][k] = a.anc[((long)b * a.N + node[blk]) * kAncWords + k];
+        }
     }
 
     bool bad = (L < 0 || L > a.max_prefix);
@@ -457,14 +485,20 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     const int p_end = tree_wg ? 0 : min(npages, p_begin + a.pps);
     const int tok_begin = p_begin * kPage;
     const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
-    if (!has_tree) ancw = u64x4{0, 0, 0, 0};
+    if (!has_tree) {
+        #pragma unroll
+        for (int blk = 0; blk < RPW; ++blk) ancw[blk] = u64x4{0, 0, 0, 0};
+    }
 
     if (tid < kAncWords) s_union[tid] = 0;
     __syncthreads();
-    if (has_tree && row_ok && kw == 0 && row % a.G == 0) {
-        #pragma unroll
-        for (int k = 0; k < kAncWords; ++k)
-            if (ancw[k]) atomicOr(&s_union[k], (unsigned long long)ancw[k]);
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        if (has_tree && row_ok[blk] && kw == 0 && (rb * RB + rloc[blk]) % a.G == 0) {
+            #pragma unroll
+            for (int k = 0; k < kAncWords; ++k)
+                if (ancw[blk][k]) atomicOr(&s_union[k], (unsigned long long)ancw[blk][k]);
+        }
     }
     int my_bad = 0;
     #pragma unroll
@@ -532,12 +566,15 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 
     const PageLanes<D> pl = page_lanes<D>(lane);
 
-    RowState<D> st;
-    #pragma unroll
-    for (int i = 0; i < DT; ++i) st.o[i] = f32x16{};
+    RowState<D> st[RPW];
     const float NEG = -__builtin_inff();
-    st.m = NEG;
-    st.l = 0.f;
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        #pragma unroll
+        for (int i = 0; i < DT; ++i) st[blk].o[i] = f32x16{};
+        st[blk].m = NEG;
+        st[blk].l = 0.f;
+    }
 
     // every load the compiler issued (Q, anc, page table) has landed: from here on
     // the only vector-memory traffic is the tile ring, counted by hand
@@ -567,7 +604,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         const int it = r * KW + kw;
         if (it < n_tiles) {
             const char* kbuf = ring + ((r % RING_R) * KW + kw) * Gm::BUF_BYTES;
-            tile_product<D>(st, kbuf, kbuf + Gm::TILE_BYTES, qreg, tile_src(it), ancw, N, scale_log2, v_off, hf, l32);
+            tile_product<D, RPW>(st, kbuf, kbuf + Gm::TILE_BYTES, qreg, tile_src(it), ancw, N, scale_log2, v_off, hf,
+                                 l32);
         }
     }
 
@@ -577,42 +615,52 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 
     // ---- one row block's result, as (m, l, unnormalised O) per row
     if constexpr (KW == 1) {
-        const float l_tot = st.l + __shfl_xor(st.l, 32);
-        if (n_act == 1) {
-            if (row_ok) {
-                const float inv = bad ? NANF : 1.f / l_tot;
-                uint16_t* op = a.out + (((long)b * a.N + node) * a.Hq + head) * D + 4 * hf;
-                #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    #pragma unroll
-                    for (int rq = 0; rq < 4; ++rq) {
-                        const u32x2 v = {pack_bf16x2(st.o[dt][4 * rq] * inv, st.o[dt][4 * rq + 1] * inv),
-                                         pack_bf16x2(st.o[dt][4 * rq + 2] * inv, st.o[dt][4 * rq + 3] * inv)};
-                        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = v;
-                    }
-                }
-                if (a.lse && hf == 0)
-                    a.lse[((long)b * a.N + node) * a.Hq + head] = bad ? NANF : (st.m + __log2f(l_tot)) * LN2;
-            }
-            return;
-        }
-        const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rloc;
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int blk = 0; blk < RPW; ++blk) {
+            const RowState<D>& sb = st[blk];
+            const float l_tot = sb.l + __shfl_xor(sb.l, 32);
+            // opaque copies: the output offset is formed here, not shared with the Q
+            // offset of the set-up and kept live (64-bit) through the tile loop
+            int nd = node[blk], hd = head[blk], h2f = hf;
+            asm volatile("" : "+v"(nd), "+v"(hd), "+v"(h2f));
+            if (n_act == 1) {
+                if (row_ok[blk]) {
+                    const float inv = bad ? NANF : 1.f / l_tot;
+                    uint16_t* op = a.out + (((long)b * a.N + nd) * a.Hq + hd) * D + 4 * h2f;
+                    #pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        #pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            const u32x2 v = {pack_bf16x2(sb.o[dt][4 * rq] * inv, sb.o[dt][4 * rq + 1] * inv),
+                                             pack_bf16x2(sb.o[dt][4 * rq + 2] * inv, sb.o[dt][4 * rq + 3] * inv)};
+                            *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = v;
+                        }
+                    }
+                    if (a.lse && h2f == 0)
+                        a.lse[((long)b * a.N + nd) * a.Hq + hd] = bad ? NANF : (sb.m + __log2f(l_tot)) * LN2;
+                }
+                continue;
+            }
+            const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rloc[blk];
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
             #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
-                st16(ro, (pr * D + dt * 32 + 8 * rq + 4 * hf) * 4, v);
+            for (int dt = 0; dt < DT; ++dt) {
+                #pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4 v = {sb.o[dt][4 * rq], sb.o[dt][4 * rq + 1], sb.o[dt][4 * rq + 2], sb.o[dt][4 * rq + 3]};
+                    st16(ro, (pr * D + dt * 32 + 8 * rq + 4 * h2f) * 4, v);
+                }
+            }
+            if (h2f == 0) {
+                const u32x2 ml = {__float_as_uint(bad ? NANF : sb.m), __float_as_uint(bad ? NANF : l_tot)};
+                st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
             }
         }
-        if (hf == 0) {
-            const u32x2 ml = {__float_as_uint(bad ? NANF : st.m), __float_as_uint(bad ? NANF : l_tot)};
-            st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
-        }
+        if (n_act == 1) return;
     } else {
-        // merge the KW key groups through LDS
-        const float l_tot = st.l + __shfl_xor(st.l, 32);
+        // merge the KW key groups through LDS (one row block per wave)
+        const RowState<D>& st0 = st[0];
+        const float l_tot = st0.l + __shfl_xor(st0.l, 32);
         __syncthreads();                               // every wave is done with the ring
         {
             char* mk = reinterpret_cast<char*>(mo) + kw * RB * D * 4;
@@ -620,13 +668,13 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             for (int dt = 0; dt < DT; ++dt) {
                 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
-                    const f32x4 v = {st.o[dt][4 * rq], st.o[dt][4 * rq + 1], st.o[dt][4 * rq + 2], st.o[dt][4 * rq + 3]};
-                    *reinterpret_cast<f32x4*>(mk + merge_off<D>(rloc, (dt * 32 + 8 * rq + 4 * hf) >> 2)) = v;
+                    const f32x4 v = {st0.o[dt][4 * rq], st0.o[dt][4 * rq + 1], st0.o[dt][4 * rq + 2], st0.o[dt][4 * rq + 3]};
+                    *reinterpret_cast<f32x4*>(mk + merge_off<D>(rloc[0], (dt * 32 + 8 * rq + 4 * hf) >> 2)) = v;
                 }
             }
             if (hf == 0) {
-                s_ml[kw][rloc][0] = st.m;
-                s_ml[kw][rloc][1] = l_tot;
+                s_ml[kw][rloc[0]][0] = st0.m;
+                s_ml[kw][rloc[0]][1] = l_tot;
             }
         }
         __syncthreads();
@@ -697,60 +745,67 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     {
         constexpr int TPR = T / RB;                // threads per row
         constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread
-        constexpr int SB = (32 / CPT) > 1 ? (32 / CPT) : 1;   // splits per batch: <= 32 float4 in flight
+        constexpr int CB = CPT < 16 ? CPT : 16;    // chunks per pass over the splits
+        constexpr int SB = (32 / CB) > 1 ? (32 / CB) : 1;   // splits per batch: <= 32 float4 in flight
         const int rl = tid / TPR, part = tid % TPR;
         const int grow = rb * RB + rl;
-        const uint32_t base = (uint32_t)item * a.splits * RB + rl;   // + sp * RB
+        const uint32_t base = (uint32_t)item * a.splits * RB + rl;   // + slot * RB
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
-        // one batch of loads (every split's m, l and O slice) per SB splits, merged
-        // with a running max so no pass has to wait for another
-        float M = NEG;
-        f32x4 acc[CPT];
-        #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float Ls = 0.f;
-        for (int sp0 = 0; sp0 < n_act; sp0 += SB) {
-            f32x4 v[SB][CPT];
-            u32x2 ml[SB];
+        const bool out_ok = grow < a.rows;
+        const int gnode = out_ok ? grow / a.G : 0, ghead = kvh * a.G + (out_ok ? grow % a.G : 0);
+        // the thread's CPT chunks in passes of CB; per pass, one batch of loads (every
+        // split's m, l and O slice) per SB splits, merged with a running max so no
+        // batch waits for another
+        for (int c0 = 0; c0 < CPT; c0 += CB) {
+            float M = NEG;
+            f32x4 acc[CB];
             #pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int kk = min(sp0 + j, n_act - 1);
-                const int slot = (a.tree_split && kk >= n_pre_splits) ? a.splits - 1 : kk;
-                const uint32_t pr = base + (uint32_t)slot * RB;
+            for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float Ls = 0.f;
+            for (int sp0 = 0; sp0 < n_act; sp0 += SB) {
+                f32x4 v[SB][CB];
+                u32x2 ml[SB];
                 #pragma unroll
-                for (int c = 0; c < CPT; ++c) v[j][c] = ld16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4);
-                ml[j] = ld8(rml, pr * 8);
-            }
-            float mb = NEG;
-            #pragma unroll
-            for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));   // clamped repeats: no change
-            const float Mn = fmaxf(M, mb);
-            const float Mn_use = (Mn == NEG) ? 0.f : Mn;
-            const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                      // M = -inf -> 0
-            Ls *= sc;
-            #pragma unroll
-            for (int c = 0; c < CPT; ++c) acc[c] *= sc;
-            #pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const float wgt = (sp0 + j < n_act) ? __builtin_amdgcn_exp2f(__uint_as_float(ml[j][0]) - Mn_use) : 0.f;
-                Ls += wgt * __uint_as_float(ml[j][1]);
+                for (int j = 0; j < SB; ++j) {
+                    const int kk = min(sp0 + j, n_act - 1);
+                    const int slot = (a.tree_split && kk >= n_pre_splits) ? a.splits - 1 : kk;
+                    const uint32_t pr = base + (uint32_t)slot * RB;
+                    #pragma unroll
+                    for (int c = 0; c < CB; ++c) v[j][c] = ld16(ro, (pr * D + (part * CPT + c0 + c) * 4) * 4);
+                    ml[j] = ld8(rml, pr * 8);
+                }
+                float mb = NEG;
                 #pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[c] += wgt * v[j][c];
+                for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));   // clamped repeats: no change
+                const float Mn = fmaxf(M, mb);
+                const float Mn_use = (Mn == NEG) ? 0.f : Mn;
+                const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                      // M = -inf -> 0
+                Ls *= sc;
+                #pragma unroll
+                for (int c = 0; c < CB; ++c) acc[c] *= sc;
+                #pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const float wgt =
+                        (sp0 + j < n_act) ? __builtin_amdgcn_exp2f(__uint_as_float(ml[j][0]) - Mn_use) : 0.f;
+                    Ls += wgt * __uint_as_float(ml[j][1]);
+                    #pragma unroll
+                    for (int c = 0; c < CB; ++c) acc[c] += wgt * v[j][c];
+                }
+                M = Mn;
             }
-            M = Mn;
-        }
-        if (grow < a.rows) {
-            const int gnode = grow / a.G, ghead = kvh * a.G + grow % a.G;
-            const float inv = 1.f / Ls;
-            uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * CPT * 4;
-            #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
-                                 pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-                *reinterpret_cast<u32x2*>(op + 4 * c) = v;
+            if (out_ok) {
+                const float inv = 1.f / Ls;
+                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + (part * CPT + c0) * 4;
+                #pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
+                                     pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+                    *reinterpret_cast<u32x2*>(op + 4 * c) = v;
+                }
+                if (a.lse && part == 0 && c0 == 0)
+                    a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
             }
-            if (a.lse && part == 0) a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
         }
     }
 }
@@ -758,7 +813,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
-    int rw, kw, rb, nrb, items, splits, pps, order, tree_split;
+    int rw, kw, rpw, rb, nrb, items, splits, pps, order, tree_split;
     long grid;
     size_t off_cnt, fill_bytes, off_ml, off_o, bytes;
 };
@@ -785,6 +840,7 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     if (rows <= 64) { p.rw = 1; p.kw = 4; }
     else if (rows <= 128) { p.rw = 4; p.kw = 2; }
     else { p.rw = 8; p.kw = 1; }   // (128-row blocks hold one prefetch round: slower)
+    p.rpw = 1;
     // tuning override: JF_RW = 1, 2, 4 or 8 row groups (key groups follow)
     switch (env_int("JF_RW", 0)) {
         case 1: p.rw = 1; p.kw = 4; break;
@@ -793,7 +849,9 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
         case 8: p.rw = 8; p.kw = 1; break;
         default: break;
     }
-    p.rb = 32 * p.rw;
+    // 256-row blocks as 4 waves x 2 row blocks (instead of 8 waves x 1): JF_RPW=2
+    if (p.rw == 8 && env_int("JF_RPW", 1) == 2) { p.rw = 4; p.kw = 1; p.rpw = 2; }
+    p.rb = 32 * p.rw * p.rpw;
     p.nrb = (int)((rows + p.rb - 1) / p.rb);
     p.items = s.B * s.Hkv * p.nrb;
     const int max_pages = (max_prefix + kPage - 1) / kPage;
@@ -847,18 +905,19 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     return p;
 }
 
-template <int D, int RW, int KW>
+template <int D, int RW, int KW, int RPW>
 static hipError_t launch_bf16_t(const AttnArgs& a, long grid, hipStream_t stream) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, RW, KW>), dim3((unsigned)grid), dim3(RW * KW * 64), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, RW, KW, RPW>), dim3((unsigned)grid), dim3(RW * KW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_bf16_d(const AttnPlanBf16& p, const AttnArgs& a, hipStream_t stream) {
-    if (p.rw == 1) return launch_bf16_t<D, 1, 4>(a, p.grid, stream);
-    if (p.rw == 2) return launch_bf16_t<D, 2, 2>(a, p.grid, stream);
-    if (p.rw == 4) return launch_bf16_t<D, 4, 2>(a, p.grid, stream);
-    return launch_bf16_t<D, 8, 1>(a, p.grid, stream);
+    if (p.rpw == 2) return launch_bf16_t<D, 4, 1, 2>(a, p.grid, stream);
+    if (p.rw == 1) return launch_bf16_t<D, 1, 4, 1>(a, p.grid, stream);
+    if (p.rw == 2) return launch_bf16_t<D, 2, 2, 1>(a, p.grid, stream);
+    if (p.rw == 4) return launch_bf16_t<D, 4, 2, 1>(a, p.grid, stream);
+    return launch_bf16_t<D, 8, 1, 1>(a, p.grid, stream);
 }
 
 hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
