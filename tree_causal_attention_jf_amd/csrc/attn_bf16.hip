@@ -10,16 +10,19 @@
 // Work decomposition
 //   * GQA packing: the G*N query rows that share one KV head form one matrix
 //     (row r = node * G + g), so every K/V tile is staged once per KV head.
-//   * A workgroup owns RB = 32 * RW consecutive rows of one (sequence, KV
-//     head) and a contiguous run of prefix pages (a "split"). The split that
-//     owns the last prefix page also runs the tree block.
+//   * A workgroup owns RB = 32 * RW * RPW rows of one (sequence, KV head) and
+//     a contiguous run of prefix pages (a "split"). The split that owns the
+//     last prefix page also runs the tree block, unless splits are short: then
+//     the tree block gets a split of its own, so that it does not add a round
+//     (and a full memory latency) to the last prefix split.
 //   * Its RW * KW waves form RW row groups (32 rows each) times KW key groups:
 //     key group k multiplies tiles k, k + KW, k + 2 KW, ... of the split, so
 //     small row counts still keep many tiles in flight per workgroup. Key
 //     groups are merged in LDS at the end.
 //   * Splits of one row block are merged in the same launch by the last one
-//     to finish (agent-scope counter), in split order, with every thread's
-//     loads in flight at once.
+//     to finish: partials are written through to device scope, one thread per
+//     workgroup bumps an agent-scope counter, and the last arriver invalidates
+//     its caches and merges the partials in split order.
 //   * Workgroup ids are remapped so that the row blocks and splits of one KV
 //     head land on one XCD and share its L2.
 //
@@ -732,7 +735,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     wait_own_stores();
     __syncthreads();
     if (tid == 0) {
-        const int old = arrive_release(&a.counters[item]);
+        const int old = arrive(&a.counters[item]);
         s_last = (old == n_act - 1);
         if (s_last) {
             reset_counter(&a.counters[item]);
@@ -885,7 +888,7 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     }
     // short splits (a few rounds each): the tree tiles get a split of their own instead
     // of adding a round (and a full memory latency) to the last prefix split
-    if (splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 0) &&
+    if (splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 1) &&
         (size_t)p.items * (splits + 1) * p.rb * s.D * 4 < (size_t)0xffffff00u) {
         p.tree_split = 1;
         splits += 1;

@@ -60,11 +60,11 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
 // result read by a workgroup on another XCD has to be pushed past the writer's
 // L2 and must not be served from a stale line of the reader's.
 //
-// Bulk results (attention partials, tens of KB per workgroup) use plain
-// stores and loads around one release / acquire pair:
-//   writer: stores, wait_own_stores() in every wave, barrier, then ONE thread
-//           calls arrive_release() (agent-scope release: this XCD's L2 is
-//           written back before the counter moves);
+// Bulk results (attention partials, tens of KB per workgroup):
+//   writer: device-scope (write-through) stores st16 / st8, wait_own_stores()
+//           in every wave, barrier, then ONE thread bumps the counter with
+//           arrive(); no cache-wide write-back is needed, and many workgroups
+//           publishing at once do not serialize on one;
 //   reader: the thread that saw the last arrival calls acquire_agent()
 //           (invalidates this CU's L1 and this XCD's L2), tells the workgroup
 //           through LDS and a barrier, and the workgroup then loads normally.
@@ -74,10 +74,6 @@ __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0
 
 __device__ __forceinline__ int arrive(int* counter) {
     return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int arrive_release(int* counter) {
-    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
@@ -91,8 +87,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
+constexpr int kDeviceScope = 16;   // buffer-instruction cache policy sc1: write through to device scope
+
 __device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScope);
 }
 
 __device__ __forceinline__ f32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -100,7 +98,7 @@ __device__ __forceinline__ f32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 __device__ __forceinline__ void st8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kDeviceScope);
 }
 
 __device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
