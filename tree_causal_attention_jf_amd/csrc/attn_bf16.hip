@@ -749,7 +749,10 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         constexpr int TPR = T / RB;                // threads per row
         constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread
         constexpr int CB = CPT < 16 ? CPT : 16;    // chunks per pass over the splits
-        constexpr int SB = (32 / CB) > 1 ? (32 / CB) : 1;   // splits per batch: <= 32 float4 in flight
+        // splits per batch: up to 32 float4 in flight per thread, 64 in the four-wave
+        // layouts (one wave per SIMD: twice the registers)
+        constexpr int INFLIGHT = NW <= 4 ? 64 : 32;
+        constexpr int SB = (INFLIGHT / CB) > 1 ? (INFLIGHT / CB) : 1;
         const int rl = tid / TPR, part = tid % TPR;
         const int grow = rb * RB + rl;
         const uint32_t base = (uint32_t)item * a.splits * RB + rl;   // + slot * RB
