@@ -67,7 +67,7 @@ struct AttnArgs {
     float* lse;
     int* counters;     // [items]                       zero between calls
     float* part_ml;    // [items][splits][RB][2]        (m in log2 units, l)
-    float* part_o;     // [items][splits][RB][D]        unnormalised
+    float* part_o;     // [items][splits] x [RB][D]     unnormalised, fragment-major (part_off)
     uint32_t part_ml_bytes, part_o_bytes;
     int B, N, Hq, Hkv, G, num_pages, max_pages, max_prefix;
     int rows;          // G * N
@@ -373,9 +373,26 @@ __device__ __forceinline__ int merge_off(int r, int c) {
     return r * (D * 4) + ((c ^ (r & 7)) << 4);
 }
 
+// Float offset of float4 chunk c (columns 4c..4c+3) of row r within one split's
+// [RB][D] partial O, in one of two layouts, each chosen so that every store
+// instruction of its producer writes whole 128-byte lines (the hand-off stores
+// write through to memory, where partial lines cost extra transactions):
+//  - fragment-major (FRAG, for the tile loop's own MFMA layout): per 32-row block
+//    and output fragment (dt, rq), 64 lanes x 16 B = 1 KB, lane = (r % 32) + 32 (c % 2);
+//  - row-major (after the key-group merge, whose threads own chunks part, part + TPR, ...).
+template <int D, bool FRAG>
+__device__ __forceinline__ uint32_t part_off(int r, int c) {
+    constexpr int DT = D / 32;
+    if constexpr (FRAG)
+        return (uint32_t)(((((r >> 5) * DT + (c >> 3)) * 4 + ((c >> 1) & 3)) * 64 + (r & 31) + 32 * (c & 1)) * 4);
+    else
+        return (uint32_t)(r * D + c * 4);
+}
+
 template <int D, int RW, int KW, int RPW>
 __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     using Gm = Geo<D>;
+    constexpr bool kFragPart = KW == 1;              // split partial layout (part_off)
     constexpr int NW = RW * KW;
     constexpr int T = NW * 64;
     constexpr int RB = RW * 32 * RPW;                // rows per workgroup: RW waves x RPW blocks of 32
@@ -644,14 +661,15 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 }
                 continue;
             }
-            const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rloc[blk];
+            const uint32_t psplit = ((uint32_t)item * a.splits + s) * RB;
+            const uint32_t pr = psplit + rloc[blk];
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
             #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
                     const f32x4 v = {sb.o[dt][4 * rq], sb.o[dt][4 * rq + 1], sb.o[dt][4 * rq + 2], sb.o[dt][4 * rq + 3]};
-                    st16(ro, (pr * D + dt * 32 + 8 * rq + 4 * h2f) * 4, v);
+                    st16(ro, (psplit * D + part_off<D, kFragPart>(rloc[blk], dt * 8 + 2 * rq + h2f)) * 4, v);
                 }
             }
             if (h2f == 0) {
@@ -662,6 +680,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         if (n_act == 1) return;
     } else {
         // merge the KW key groups through LDS (one row block per wave)
+        constexpr int TPR = T / RB;                 // threads per row
+        constexpr int CPT = D / 4 / TPR;            // float4 chunks per thread
         const RowState<D>& st0 = st[0];
         const float l_tot = st0.l + __shfl_xor(st0.l, 32);
         __syncthreads();                               // every wave is done with the ring
@@ -672,7 +692,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
                     const f32x4 v = {st0.o[dt][4 * rq], st0.o[dt][4 * rq + 1], st0.o[dt][4 * rq + 2], st0.o[dt][4 * rq + 3]};
-                    *reinterpret_cast<f32x4*>(mk + merge_off<D>(rloc[0], (dt * 32 + 8 * rq + 4 * hf) >> 2)) = v;
+                    *reinterpret_cast<f32x4*>(mk + merge_off<D>(rloc[0], dt * 8 + 2 * rq + hf)) = v;
                 }
             }
             if (hf == 0) {
@@ -681,8 +701,6 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             }
         }
         __syncthreads();
-        constexpr int TPR = T / RB;                 // threads per row
-        constexpr int CPT = D / 4 / TPR;            // float4 chunks per thread
         const int rl = tid / TPR, part = tid % TPR;
         const int grow = rb * RB + rl;
         float M = NEG;
@@ -696,6 +714,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             wk[k] = __builtin_amdgcn_exp2f(s_ml[k][rl][0] - M_use);
             Ls += wk[k] * s_ml[k][rl][1];
         }
+        // the thread's chunks are part, part + TPR, ...: each pass over c reads and
+        // writes whole lines
         f32x4 acc[CPT];
         #pragma unroll
         for (int c = 0; c < CPT; ++c) {
@@ -703,28 +723,29 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             #pragma unroll
             for (int k = 0; k < KW; ++k)
                 acc[c] += wk[k] * *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(mo) + k * RB * D * 4 +
-                                                                  merge_off<D>(rl, part * CPT + c));
+                                                                  merge_off<D>(rl, c * TPR + part));
         }
         if (n_act == 1) {
             if (grow < a.rows) {
                 const int gnode = grow / a.G, ghead = kvh * a.G + grow % a.G;
                 const float inv = bad ? NANF : 1.f / Ls;
-                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * CPT * 4;
+                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * 4;
                 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
                     const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
                                      pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + 4 * c) = v;
+                    *reinterpret_cast<u32x2*>(op + 4 * TPR * c) = v;
                 }
                 if (a.lse && part == 0)
                     a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = bad ? NANF : (M + __log2f(Ls)) * LN2;
             }
             return;
         }
-        const uint32_t pr = ((uint32_t)item * a.splits + s) * RB + rl;
+        const uint32_t psplit = ((uint32_t)item * a.splits + s) * RB;
+        const uint32_t pr = psplit + rl;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         #pragma unroll
-        for (int c = 0; c < CPT; ++c) st16(ro, (pr * D + part * CPT * 4 + 4 * c) * 4, acc[c]);
+        for (int c = 0; c < CPT; ++c) st16(ro, (psplit * D + part_off<D, kFragPart>(rl, c * TPR + part)) * 4, acc[c]);
         if (part == 0) {
             const u32x2 ml = {__float_as_uint(bad ? NANF : M), __float_as_uint(bad ? NANF : Ls)};
             st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
@@ -755,7 +776,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         constexpr int SB = (INFLIGHT / CB) > 1 ? (INFLIGHT / CB) : 1;
         const int rl = tid / TPR, part = tid % TPR;
         const int grow = rb * RB + rl;
-        const uint32_t base = (uint32_t)item * a.splits * RB + rl;   // + slot * RB
+        const uint32_t base = (uint32_t)item * a.splits * RB;        // + slot * RB
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
         const bool out_ok = grow < a.rows;
@@ -776,10 +797,10 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 for (int j = 0; j < SB; ++j) {
                     const int kk = min(sp0 + j, n_act - 1);
                     const int slot = (a.tree_split && kk >= n_pre_splits) ? a.splits - 1 : kk;
-                    const uint32_t pr = base + (uint32_t)slot * RB;
+                    const uint32_t ps = base + (uint32_t)slot * RB;
                     #pragma unroll
-                    for (int c = 0; c < CB; ++c) v[j][c] = ld16(ro, (pr * D + (part * CPT + c0 + c) * 4) * 4);
-                    ml[j] = ld8(rml, pr * 8);
+                    for (int c = 0; c < CB; ++c) v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
+                    ml[j] = ld8(rml, (ps + rl) * 8);
                 }
                 float mb = NEG;
                 #pragma unroll
@@ -802,12 +823,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             }
             if (out_ok) {
                 const float inv = 1.f / Ls;
-                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + (part * CPT + c0) * 4;
+                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + (c0 * TPR + part) * 4;
                 #pragma unroll
                 for (int c = 0; c < CB; ++c) {
                     const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
                                      pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + 4 * c) = v;
+                    *reinterpret_cast<u32x2*>(op + 4 * TPR * c) = v;
                 }
                 if (a.lse && part == 0 && c0 == 0)
                     a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
