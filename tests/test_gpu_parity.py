@@ -244,21 +244,40 @@ def test_attention_bf16_small(jf, case, unscaled):
     check_bf16(out, ref, lse, lref, f"{name}{' unscaled' if unscaled else ''}", abs_tol=derived_bf16_bar(wl))
 
 
+@pytest.mark.parametrize("balanced", [1, 0])
 @pytest.mark.parametrize("rw,splits,rpw", [(1, 1, 1), (1, 7, 1), (2, 3, 1), (4, 5, 1), (8, 2, 1), (8, 64, 1),
                                             (4, 0, 1), (8, 1, 2), (8, 3, 2), (8, 64, 2)])
-def test_attention_bf16_forced_plans(jf, rw, splits, rpw, monkeypatch):
+def test_attention_bf16_forced_plans(jf, rw, splits, rpw, balanced, monkeypatch):
     # every row-group layout (rpw 2: four waves of two 32-row blocks), with the
     # prefix cut into several splits merged by the last one to finish (including
-    # more splits than some sequences have tiles)
+    # more splits than some sequences have tiles); balanced 1: the kernel cuts
+    # every sequence into that many pieces itself and deals them out longest
+    # first, 0: uniform page ranges in id order
     monkeypatch.setenv("JF_RW", str(rw))
     monkeypatch.setenv("JF_SPLITS", str(splits))
     monkeypatch.setenv("JF_RPW", str(rpw))
+    monkeypatch.setenv("JF_BALANCED", str(balanced))
     for D, Hq, Hkv in ((128, 8, 2), (64, 16, 2)):
         wl = W.make_workload("c1_chain16", 5, with_accept=False, B=4, N=150, prefix=("list", [700, 0, 1, 2100]),
                              Hq=Hq, Hkv=Hkv, D=D, tree=("random", 9))
         out, lse = run_attention(jf, wl, to_dev(wl))
         ref, lref = _oracle_full(wl)
-        check_bf16(out, ref, lse, lref, f"rw {rw} splits {splits} rpw {rpw} D {D}", abs_tol=derived_bf16_bar(wl))
+        check_bf16(out, ref, lse, lref, f"rw {rw} splits {splits} rpw {rpw} balanced {balanced} D {D}",
+                   abs_tol=derived_bf16_bar(wl))
+
+
+@pytest.mark.parametrize("lens", [[3000, 100, 200, 50, 2500, 10], [4000, 0, 17, 4000, 1, 900, 64, 3999]],
+                         ids=["skewed6", "skewed8"])
+def test_attention_bf16_balanced_skewed(jf, lens):
+    # skewed prefix lengths, default plan: the kernel cuts the long sequences into
+    # pieces from the lengths it reads (the host sees only the longest) and leaves
+    # the short ones whole; unused workgroup ids exit
+    for D, Hq, Hkv, N in ((128, 8, 2, 64), (64, 16, 4, 40)):
+        wl = W.make_workload("c1_chain16", 17, with_accept=False, B=len(lens), N=N, prefix=("list", lens),
+                             Hq=Hq, Hkv=Hkv, D=D, tree=("random", 7))
+        out, lse = run_attention(jf, wl, to_dev(wl))
+        ref, lref = _oracle_full(wl)
+        check_bf16(out, ref, lse, lref, f"lens {lens} D {D}", abs_tol=derived_bf16_bar(wl))
 
 
 def test_one_workspace_serves_every_shape(jf, monkeypatch):

@@ -23,8 +23,15 @@
 //     to finish: partials are written through to device scope, one thread per
 //     workgroup bumps an agent-scope counter, and the last arriver invalidates
 //     its caches and merges the partials in split order.
-//   * Workgroup ids are remapped so that the row blocks and splits of one KV
-//     head land on one XCD and share its L2.
+//   * Schedules. One sequence: every (KV head, row block) gets the same number
+//     of equal page ranges, and workgroup ids are remapped so that one KV
+//     head's row blocks and splits land on one XCD and share its L2. Batches of
+//     2..64 sequences: each workgroup plans from the prefix lengths themselves
+//     (the host knows only the longest). A sequence with more than 1.5x the
+//     mean work per CU is cut into ceil(work / mean) pieces; units (sequence,
+//     piece, KV head) are ranked by piece size and dealt round robin to the
+//     XCDs, a unit's row blocks together, so that every XCD list-schedules its
+//     own longest-first share.
 //
 // Data movement: 64-key tiles of K and V go from HBM straight into a 4-tile
 // LDS ring with global_load_lds_dwordx4 (16 bytes per lane, no staging
@@ -52,7 +59,7 @@ constexpr int kKeyTile = 64;
 constexpr int kRing = 4;                 // LDS tile buffers
 constexpr int kMaxPagesPerSplit = 1024;
 constexpr int kMaxSplits = 64;
-constexpr int kMaxOrdered = 64;          // batches ranked by prefix length inside the kernel
+constexpr int kMaxBalanced = 64;         // batches planned from their prefix lengths inside the kernel (one wave)
 
 struct AttnArgs {
     const uint16_t* q;
@@ -73,8 +80,11 @@ struct AttnArgs {
     int rows;          // G * N
     int nrb;           // row blocks per (sequence, KV head)
     int splits;        // splits per row block in the grid
-    int pps;           // prefix pages per split (multiple of 4)
-    int order;         // 1: walk the sequences longest first (B <= kMaxOrdered)
+    int pps;           // prefix pages per split (multiple of 4; per sequence when balanced)
+    int balanced;      // 1: per-sequence pieces, units dealt longest first to the XCDs (2 <= B <= kMaxBalanced)
+    int tree_tiles;    // 64-key tiles of the tree (for the balanced plan's work estimate)
+    int cus;           // compute units of the device (ditto)
+    int forced;        // balanced: every sequence takes `splits` pieces (tuning and tests)
     int tree_split;    // 1: split splits-1 runs the tree tiles alone, the others the prefix
     float scale_log2;  // sm_scale * log2(e)
 };
@@ -408,37 +418,77 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     __shared__ float s_ml[KW][RB][2];
     __shared__ unsigned long long s_union[kAncWords];
     __shared__ int s_last;
-    __shared__ int s_seq;
+    __shared__ int s_plan[4];
+    __shared__ int s_epi[5];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index: uniform
 
-    // ---- which (sequence, KV head, split, row block) this workgroup owns. Workgroups
-    // start in id order as CUs free up; with `order`, the ids walk the sequences from
-    // the longest prefix to the shortest, so short work fills in at the end.
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int rb = lid % a.nrb;
-    int t1 = lid / a.nrb;
-    const int s = t1 % a.splits;
-    t1 /= a.splits;
-    const int kvh = t1 % a.Hkv;
-    int b = t1 / a.Hkv;
-    if (a.order) {
+    // ---- which (sequence, KV head, split, row block) this workgroup owns
+    int rb, s, kvh, b, pps;
+    if (a.balanced) {
+        // Balanced schedule, planned alike by every workgroup from the prefix lengths:
+        //  * a sequence whose work (prefix tiles + tree tiles) exceeds 1.5x the mean
+        //    work per CU is cut into ceil(work / mean) pieces (at most `splits`) of
+        //    equal page counts;
+        //  * units (sequence, piece, KV head) are ranked by piece size, largest first,
+        //    and dealt round robin to the XCDs; a unit's nrb row blocks (which read
+        //    the same K/V pages) run one after another on one XCD.
+        // Each XCD starts its workgroups in id order as its CUs free up, so it
+        // list-schedules its own longest-first share. Ids past the units are idle.
         if (w == 0) {
-            // rank of sequence `lane` = number of sequences before it (longer, or as
-            // long with a smaller index); the sequence of rank b is ours
-            const int Lm = lane < a.B ? a.prefix_len[lane] : -1;
-            int rank = 0;
+            const int Lm = lane < a.B ? a.prefix_len[lane] : 0;
+            const int pg = (lane < a.B && Lm > 0 && Lm <= a.max_prefix) ? (Lm + kPage - 1) / kPage : 0;
+            const int tiles = (pg + 3) / 4 + a.tree_tiles;
+            int tot = lane < a.B ? tiles : 0;
+            #pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+            const float mean = (float)tot * (float)(a.Hkv * a.nrb) / (float)a.cus;
+            int n = 1;
+            if (a.forced) n = a.splits;
+            else if (mean > 0.f && (float)tiles > 1.5f * mean) n = min(a.splits, (int)ceilf((float)tiles / mean));
+            n = min(n, max(1, pg / (4 * KW)));                            // a full round of tiles per piece
+            n = max(n, (pg + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);  // (the host keeps this <= splits)
+            int pp = (pg + n - 1) / n;
+            pp = max(4, (pp + 3) / 4 * 4);
+            n = lane < a.B ? max(1, (pg + pp - 1) / pp) : 0;
+            const int key = lane < a.B ? min(pp, pg) : -1;
+            int off = 0;                               // units of the sequences ranked before this one
             for (int j = 0; j < a.B; ++j) {
-                const int Lj = __shfl(Lm, j);
-                rank += (Lj > Lm || (Lj == Lm && j < lane)) ? 1 : 0;
+                const int kj = __shfl(key, j), nj = __shfl(n, j);
+                off += (kj > key || (kj == key && j < lane)) ? nj : 0;
             }
-            if (lane < a.B && rank == b) s_seq = lane;
+            const int slot = blockIdx.x / kNumXcd;
+            const int u = (slot / a.nrb) * kNumXcd + blockIdx.x % kNumXcd;
+            const int lo = off * a.Hkv;
+            const bool mine = lane < a.B && u >= lo && u < lo + n * a.Hkv;
+            if (mine) {
+                s_plan[0] = lane;
+                s_plan[1] = (u - lo) / a.Hkv;
+                s_plan[2] = (u - lo) % a.Hkv;
+                s_plan[3] = pp;
+            }
+            if (__ballot(mine) == 0 && lane == 0) s_plan[0] = -1;
         }
         __syncthreads();
-        b = __builtin_amdgcn_readfirstlane(s_seq);
+        b = __builtin_amdgcn_readfirstlane(s_plan[0]);
+        if (b < 0) return;                             // idle id (whole workgroup)
+        s = __builtin_amdgcn_readfirstlane(s_plan[1]);
+        kvh = __builtin_amdgcn_readfirstlane(s_plan[2]);
+        pps = __builtin_amdgcn_readfirstlane(s_plan[3]);
+        rb = (blockIdx.x / kNumXcd) % a.nrb;
+    } else {
+        // ids remapped so that one KV head's row blocks and splits share an XCD
+        const int lid = xcd_remap(blockIdx.x, gridDim.x);
+        rb = lid % a.nrb;
+        int t1 = lid / a.nrb;
+        s = t1 % a.splits;
+        t1 /= a.splits;
+        kvh = t1 % a.Hkv;
+        b = t1 / a.Hkv;
+        pps = a.pps;
     }
-    const int item = (b * a.Hkv + kvh) * a.nrb + rb;
+    int item = (b * a.Hkv + kvh) * a.nrb + rb;
     const int rw = w % RW, kw = w / RW;
     const int hf = lane >> 5, l32 = lane & 31;
     // the lane's row in each of the wave's row blocks
@@ -459,8 +509,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     constexpr int PPT = (kMaxPagesPerSplit + T - 1) / T;
     // with tree_split, the last split slot holds no prefix pages
     const bool tree_wg = a.tree_split && s == a.splits - 1;
-    const int p_begin = tree_wg ? 0 : s * a.pps;
-    const int p_avail = tree_wg ? 0 : min(a.pps, a.max_pages - p_begin);
+    const int p_begin = tree_wg ? 0 : s * pps;
+    const int p_avail = tree_wg ? 0 : min(pps, a.max_pages - p_begin);
     int L = a.prefix_len[b];
     int pid[PPT];
     #pragma unroll
@@ -490,7 +540,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     const int npages = (L + kPage - 1) / kPage;
     // splits that hold work: the prefix splits, and the tree either in the last of
     // them or (tree_split) in its own slot, splits - 1
-    const int n_pre_splits = (npages + a.pps - 1) / a.pps;
+    const int n_pre_splits = (npages + pps - 1) / pps;
     int n_act;
     bool has_tree;
     if (a.tree_split) {
@@ -502,7 +552,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         if (s >= n_act) return;
         has_tree = (s == n_act - 1);
     }
-    const int p_end = tree_wg ? 0 : min(npages, p_begin + a.pps);
+    const int p_end = tree_wg ? 0 : min(npages, p_begin + pps);
     const int tok_begin = p_begin * kPage;
     const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
     if (!has_tree) {
@@ -532,6 +582,15 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             }
             s_pages[i] = v;
         }
+    }
+    // the coordinates only the epilogue needs go to LDS and are read back there,
+    // rather than held in registers through the tile loop
+    if (tid == 0) {
+        s_epi[0] = item;
+        s_epi[1] = s;
+        s_epi[2] = rb;
+        s_epi[3] = n_act;
+        s_epi[4] = n_pre_splits;
     }
     bad = __syncthreads_or(my_bad) || bad;
 
@@ -629,6 +688,11 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         }
     }
 
+    item = __builtin_amdgcn_readfirstlane(s_epi[0]);
+    s = __builtin_amdgcn_readfirstlane(s_epi[1]);
+    rb = __builtin_amdgcn_readfirstlane(s_epi[2]);
+    n_act = __builtin_amdgcn_readfirstlane(s_epi[3]);
+    const int n_pre_e = __builtin_amdgcn_readfirstlane(s_epi[4]);
     const float NANF = __builtin_nanf("");
     const float LN2 = 0.69314718055994530942f;
     float* mo = reinterpret_cast<float*>(ring);      // key-group merge area (reuses the ring)
@@ -796,7 +860,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 #pragma unroll
                 for (int j = 0; j < SB; ++j) {
                     const int kk = min(sp0 + j, n_act - 1);
-                    const int slot = (a.tree_split && kk >= n_pre_splits) ? a.splits - 1 : kk;
+                    const int slot = (a.tree_split && kk >= n_pre_e) ? a.splits - 1 : kk;
                     const uint32_t ps = base + (uint32_t)slot * RB;
                     #pragma unroll
                     for (int c = 0; c < CB; ++c) v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
@@ -840,7 +904,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
-    int rw, kw, rpw, rb, nrb, items, splits, pps, order, tree_split;
+    int rw, kw, rpw, rb, nrb, items, splits, pps, balanced, forced, tree_split, cus;
     long grid;
     size_t off_cnt, fill_bytes, off_ml, off_o, bytes;
 };
@@ -884,6 +948,7 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     const int max_pages = (max_prefix + kPage - 1) / kPage;
     // one workgroup per CU (the LDS ring takes most of it): aim at filling 256 CUs
     const int target = env_int("JF_TARGET_WG", 256);
+    p.cus = target > 0 ? target : 256;
     // at least one full round of tiles per split
     const int min_pages = 4 * p.kw;
     int splits = p.items > 0 ? (target + p.items - 1) / p.items : 1;
@@ -910,16 +975,27 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
         p.pps = pps;
         p.grid = (long)p.items * splits;
     }
+    // batches of 2..kMaxBalanced sequences: the kernel cuts each sequence into pieces
+    // from the actual lengths (the host knows only the longest) and deals the
+    // pieces out longest first; partial slots for up to max(splits, 2) pieces
+    if (s.B >= 2 && s.B <= kMaxBalanced && env_int("JF_BALANCED", 1)) {
+        int smax = splits > 1 ? splits : (max_splits >= 2 ? 2 : 1);
+        if ((size_t)p.items * smax * p.rb * s.D * 4 >= (size_t)0xffffff00u) smax = splits;
+        p.balanced = 1;
+        p.forced = forced > 0 ? 1 : 0;
+        p.splits = splits = smax;
+        const long units = (long)s.B * s.Hkv * smax;
+        p.grid = (units + kNumXcd - 1) / kNumXcd * kNumXcd * p.nrb;
+    }
     // short splits (a few rounds each): the tree tiles get a split of their own instead
     // of adding a round (and a full memory latency) to the last prefix split
-    if (splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 1) &&
+    if (!p.balanced && splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 1) &&
         (size_t)p.items * (splits + 1) * p.rb * s.D * 4 < (size_t)0xffffff00u) {
         p.tree_split = 1;
         splits += 1;
         p.splits = splits;
         p.grid = (long)p.items * splits;
     }
-    p.order = (s.B > 1 && s.B <= kMaxOrdered && p.grid > 256) ? 1 : 0;
     if (splits > 1) {
         // counters: the fixed region of every workspace (self-cleaning), extended past
         // it, and zero-filled before the launch, only for more than kMaxCounters items
@@ -982,7 +1058,10 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.nrb = p.nrb;
     a.splits = p.splits;
     a.pps = p.pps;
-    a.order = p.order;
+    a.balanced = p.balanced;
+    a.forced = p.forced;
+    a.tree_tiles = (s.N + kKeyTile - 1) / kKeyTile;
+    a.cus = p.cus;
     a.tree_split = p.tree_split;
     if (p.splits > 1 && p.fill_bytes > 0) {
         const int n = (int)(p.fill_bytes / 4);
