@@ -562,12 +562,23 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 
     if (tid < kAncWords) s_union[tid] = 0;
     __syncthreads();
-    #pragma unroll
-    for (int blk = 0; blk < RPW; ++blk) {
-        if (has_tree && row_ok[blk] && kw == 0 && (rb * RB + rloc[blk]) % a.G == 0) {
+    // union of the block's ancestor sets: OR over the wave's 32 rows (both half-waves
+    // hold the same rows; rows past the end hold zero), then one LDS atomic per word
+    // and wave instead of one per row
+    if (has_tree && kw == 0) {
+        #pragma unroll
+        for (int k = 0; k < kAncWords; ++k) {
+            uint64_t u = ancw[0][k];
             #pragma unroll
-            for (int k = 0; k < kAncWords; ++k)
-                if (ancw[blk][k]) atomicOr(&s_union[k], (unsigned long long)ancw[blk][k]);
+            for (int blk = 1; blk < RPW; ++blk) u |= ancw[blk][k];
+            uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+            #pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                lo |= __shfl_xor(lo, o);
+                hi |= __shfl_xor(hi, o);
+            }
+            const unsigned long long word = ((unsigned long long)hi << 32) | lo;
+            if (lane == 0 && word) atomicOr(&s_union[k], word);
         }
     }
     int my_bad = 0;
@@ -859,16 +870,23 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 u32x2 ml[SB];
                 #pragma unroll
                 for (int j = 0; j < SB; ++j) {
-                    const int kk = min(sp0 + j, n_act - 1);
-                    const int slot = (a.tree_split && kk >= n_pre_e) ? a.splits - 1 : kk;
-                    const uint32_t ps = base + (uint32_t)slot * RB;
-                    #pragma unroll
-                    for (int c = 0; c < CB; ++c) v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
-                    ml[j] = ld8(rml, (ps + rl) * 8);
+                    const int kk = sp0 + j;
+                    if (kk < n_act) {                  // uniform: slots past the last split load nothing
+                        const int slot = (a.tree_split && kk >= n_pre_e) ? a.splits - 1 : kk;
+                        const uint32_t ps = base + (uint32_t)slot * RB;
+                        #pragma unroll
+                        for (int c = 0; c < CB; ++c)
+                            v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
+                        ml[j] = ld8(rml, (ps + rl) * 8);
+                    } else {
+                        #pragma unroll
+                        for (int c = 0; c < CB; ++c) v[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        ml[j] = u32x2{__float_as_uint(NEG), 0u};
+                    }
                 }
                 float mb = NEG;
                 #pragma unroll
-                for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));   // clamped repeats: no change
+                for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));
                 const float Mn = fmaxf(M, mb);
                 const float Mn_use = (Mn == NEG) ? 0.f : Mn;
                 const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                      // M = -inf -> 0
