@@ -260,6 +260,18 @@ struct RowState {
     float l;             // partial sum of this half-wave's keys
 };
 
+// x = keep ? x : -inf, bitwise (keep is all ones or zero), in x's own register
+__device__ __forceinline__ float keep_or_neg(float x, uint32_t keep) {
+    float y;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(y) : "v"(keep), "0"(x), "s"(0xff800000u));
+    return y;
+}
+
+// all ones when bit `sh` of w is set, else zero
+__device__ __forceinline__ uint32_t bit_mask(uint32_t w, int sh) {
+    return (uint32_t)__builtin_amdgcn_sbfe((int)w, sh, 1);
+}
+
 // Multiply one 64-key tile into a wave's running state.
 // Multiply one 64-key tile into the running state of a wave's RPW row blocks
 // (32 query rows each). Every K and V operand read from LDS feeds the product
@@ -273,17 +285,45 @@ __device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, 
     constexpr int DCH = D / 16;
     constexpr int DT = D / 32;
     const float NEG = -__builtin_inff();
-    // S^T = K Q^T for two 32-key halves, per row block
+    // S^T = K Q^T for two 32-key halves, per row block. The ragged prefix tail
+    // starts the accumulators at -inf for keys past the prefix end (their rows
+    // were redirected to a valid finite key, so -inf + finite stays -inf); every
+    // other tile starts from the inline zero. Only the first k-step differs, so
+    // both paths leave their scores in the same MFMA result registers.
     f32x16 sacc[RPW][2];
+    auto kfrag = [&](int c, int h2) {
+        const int key = h2 * 32 + l32;
+        return *reinterpret_cast<const bf16x8*>(kbuf + key * Gm::ROW_BYTES + (((2 * c + hf) ^ swz_k<D>(key)) << 4));
+    };
+    {
+        const bf16x8 k0 = kfrag(0, 0), k1 = kfrag(0, 1);
+        if (!src.tree && src.t0 + kKeyTile > src.limit) {
+            const int nvalid = src.limit - src.t0 - 4 * hf;
+            f32x16 b0, b1;
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + (r & 3);
+                b0[r] = kk < nvalid ? 0.f : NEG;
+                b1[r] = kk + 32 < nvalid ? 0.f : NEG;
+            }
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk) {
+                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[blk][0], b0, 0, 0, 0);
+                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[blk][0], b1, 0, 0, 0);
+            }
+        } else {
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk) {
+                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[blk][0], f32x16{}, 0, 0, 0);
+                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[blk][0], f32x16{}, 0, 0, 0);
+            }
+        }
+    }
     #pragma unroll
-    for (int blk = 0; blk < RPW; ++blk) sacc[blk][0] = sacc[blk][1] = f32x16{};
-    #pragma unroll
-    for (int c = 0; c < DCH; ++c) {
+    for (int c = 1; c < DCH; ++c) {
         #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const int key = h2 * 32 + l32;
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbuf + key * Gm::ROW_BYTES +
-                                                               (((2 * c + hf) ^ swz_k<D>(key)) << 4));
+            const bf16x8 kf = kfrag(c, h2);
             #pragma unroll
             for (int blk = 0; blk < RPW; ++blk)
                 sacc[blk][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[blk][c], sacc[blk][h2], 0, 0, 0);
@@ -293,6 +333,8 @@ __device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, 
     #pragma unroll
     for (int blk = 0; blk < RPW; ++blk) {
         // register r of half h2 holds key h2*32 + 8*(r/4) + 4*hf + r%4 of the tile
+        // masked scores become -inf in place (same registers), so the unmasked path
+        // needs no copies where the paths meet
         if (src.tree) {
             const int tt = src.t0 / kKeyTile;
             const int left = N - src.t0;
@@ -303,16 +345,8 @@ __device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, 
             #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int sh = 8 * (r >> 2) + (r & 3);
-                if (!((lo >> sh) & 1u)) sacc[blk][0][r] = NEG;
-                if (!((hi >> sh) & 1u)) sacc[blk][1][r] = NEG;
-            }
-        } else if (src.t0 + kKeyTile > src.limit) {
-            const int nvalid = src.limit - src.t0 - 4 * hf;
-            #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = 8 * (r >> 2) + (r & 3);
-                if (kk >= nvalid) sacc[blk][0][r] = NEG;
-                if (kk + 32 >= nvalid) sacc[blk][1][r] = NEG;
+                sacc[blk][0][r] = keep_or_neg(sacc[blk][0][r], bit_mask(lo, sh));
+                sacc[blk][1][r] = keep_or_neg(sacc[blk][1][r], bit_mask(hi, sh));
             }
         }
         // online softmax (log2 domain), lazy rescale
