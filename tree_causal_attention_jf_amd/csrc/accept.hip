@@ -364,7 +364,10 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 AcceptPlan plan_accept(int B, int N, int vocab) {
     AcceptPlan p{};
     const long rows = (long)B * N;
-    const int min_chunk = 8192;                        // >= 32 values (4 loads) per thread
+    // >= 128 values (4 batches of 4 loads) per thread: every workgroup of a sequence
+    // arrives on that sequence's one counter, so fewer, longer chunks contend less
+    // (16 rows x 151936: 304 workgroups 10.6 us, 80 workgroups 9.4 us)
+    const int min_chunk = 32768;
     int chunks = (int)((1024 + rows - 1) / (rows > 0 ? rows : 1));   // aim for ~1024 workgroups
     const int max_chunks = (vocab + min_chunk - 1) / min_chunk;
     chunks = chunks < 1 ? 1 : chunks;
