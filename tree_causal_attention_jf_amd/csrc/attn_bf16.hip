@@ -539,7 +539,9 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
 
     // ---- every global read of the set-up is issued at once: the prefix length,
     // this split's block-table entries (the page range does not depend on the
-    // length), the wave's Q rows and the rows' ancestor words
+    // length), the rows' ancestor words and, last, the wave's Q rows: the page list
+    // and the tree-tile union need the first ones before the first tiles are
+    // requested, Q only once the first tile has landed
     constexpr int PPT = (kMaxPagesPerSplit + T - 1) / T;
     // with tree_split, the last split slot holds no prefix pages
     const bool tree_wg = a.tree_split && s == a.splits - 1;
@@ -552,22 +554,27 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         const int i = tid + k * T;
         pid[k] = (i < p_avail) ? a.block_table[(long)b * a.max_pages + p_begin + i] : 0;
     }
-    bf16x8 qreg[RPW][DCH];
+    // rows past the end read node 0 (a valid address): the loads stay unconditional,
+    // so the compiler's wait for the ancestor words does not have to cover the Q
+    // loads issued after them. Such a row computes node 0's prefix attention (its
+    // ancestor words are cleared below) and is never written out.
     u64x4 ancw[RPW];
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        #pragma unroll
+        for (int k = 0; k < kAncWords; ++k) ancw[blk][k] = a.anc[((long)b * a.N + node[blk]) * kAncWords + k];
+    }
+    asm volatile("" ::: "memory");                 // keep the Q loads behind the ones above
+    bf16x8 qreg[RPW][DCH];
     #pragma unroll
     for (int blk = 0; blk < RPW; ++blk) {
         const uint16_t* qp = a.q + (((long)b * a.N + node[blk]) * a.Hq + head[blk]) * D + 8 * hf;
         #pragma unroll
-        for (int c = 0; c < DCH; ++c) {
-            const u32x4 v = row_ok[blk] ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
-            qreg[blk][c] = __builtin_bit_cast(bf16x8, v);
-        }
-        ancw[blk] = u64x4{0, 0, 0, 0};
-        if (row_ok[blk]) {
-            #pragma unroll
-            for (int k = 0; k < kAncWords; ++k) ancw[blk][k] = a.anc[((long)b * a.N + node[blk]) * kAncWords + k];
-        }
+        for (int c = 0; c < DCH; ++c) qreg[blk][c] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * c));
     }
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk)
+        if (!row_ok[blk]) ancw[blk] = u64x4{0, 0, 0, 0};
 
     bool bad = (L < 0 || L > a.max_prefix);
     if (bad) L = 0;
@@ -700,11 +707,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         st[blk].l = 0.f;
     }
 
-    // every load the compiler issued (Q, anc, page table) has landed: from here on
-    // the only vector-memory traffic is the tile ring, counted by hand
-    __builtin_amdgcn_s_waitcnt(0);
-
     if constexpr (RING_R >= 2) {
+        // every load the compiler issued (Q, anc, page table) has landed: from here on
+        // the only vector-memory traffic is the tile ring, counted by hand. (Issuing the
+        // prologue rounds before this wait, beside the Q loads, measured slower for the
+        // multi-round rings.)
+        __builtin_amdgcn_s_waitcnt(0);
         // prologue: RING_R - 1 rounds in flight
         #pragma unroll
         for (int p = 0; p < RING_R - 1; ++p)
@@ -712,6 +720,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, p * KW, n_tiles, b, kvh, s_pages, pl,
                                     ring0 + p * KW * Gm::BUF_BYTES, w * DPR, lane);
     }
+    // (a one-round ring issues each round and waits for all of it, which also covers
+    // the set-up loads still landing from before its first round)
     for (int r = 0; r < n_rounds; ++r) {
         if constexpr (RING_R >= 2) {
             wait_rounds<DPR>(min(n_rounds - 1 - r, RING_R - 2));
