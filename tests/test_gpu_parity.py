@@ -352,6 +352,23 @@ def test_attention_bf16_large_sampled(jf, name):
         assert torch.isfinite(out.float()).all()
 
 
+def test_attention_bf16_batch_with_long_prefix(jf):
+    # a batch whose longest prefix needs more than one split's page list (1024 pages):
+    # the balanced plan must give that sequence at least ceil(pages / 1024) pieces
+    # whatever the work estimate says, next to short and empty prefixes
+    for lens in ([20000, 100, 5000], [16400, 0, 16384, 3]):
+        wl = W.make_workload("c1_chain16", 23, with_accept=False, B=len(lens), N=24, prefix=("list", lens),
+                             Hq=8, Hkv=2, D=128, tree=("random", 6))
+        out, lse = run_attention(jf, wl, to_dev(wl))
+        rows = _sampled_rows(wl, 40, 3) + [(0, wl.N - 1, 0), (2, 5, 7)]
+        rows = sorted(set(rows))
+        ref, lref = _oracle_full(wl, rows=rows)
+        idx = tuple(np.array(rows).T)
+        check_bf16(torch.from_numpy(out.float().cpu().numpy()[idx]), ref[idx], lse.cpu()[idx], lref[idx],
+                   f"lens {lens} ({len(rows)} rows)", abs_tol=derived_bf16_bar(wl))
+        assert torch.isfinite(out.float()).all()
+
+
 def test_attention_bf16_poison_unused_slots(jf):
     kw = dict(B=2, N=50, prefix=("list", [37, 201]), Hq=8, Hkv=2, D=128, tree=("random", 6), extra_pages=5)
     clean = W.make_workload("c1_chain16", 21, with_accept=False, **kw)

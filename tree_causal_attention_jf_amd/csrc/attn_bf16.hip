@@ -85,6 +85,7 @@ struct AttnArgs {
     int tree_tiles;    // 64-key tiles of the tree (for the balanced plan's work estimate)
     int cus;           // compute units of the device (ditto)
     int forced;        // balanced: every sequence takes `splits` pieces (tuning and tests)
+    float cut;         // balanced: a sequence is cut when its work exceeds cut x the mean per CU
     int tree_split;    // 1: split splits-1 runs the tree tiles alone, the others the prefix
     float scale_log2;  // sm_scale * log2(e)
 };
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             const float mean = (float)tot * (float)(a.Hkv * a.nrb) / (float)a.cus;
             int n = 1;
             if (a.forced) n = a.splits;
-            else if (mean > 0.f && (float)tiles > 1.5f * mean) n = min(a.splits, (int)ceilf((float)tiles / mean));
+            else if (mean > 0.f && (float)tiles > a.cut * mean) n = min(a.splits, (int)ceilf((float)tiles / mean));
             n = min(n, max(1, pg / (4 * KW)));                            // a full round of tiles per piece
             n = max(n, (pg + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);  // (the host keeps this <= splits)
             int pp = (pg + n - 1) / n;
@@ -1124,6 +1125,10 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.forced = p.forced;
     a.tree_tiles = (s.N + kKeyTile - 1) / kKeyTile;
     a.cus = p.cus;
+    {
+        const char* v = getenv("JF_BAL_CUT");
+        a.cut = (v && *v) ? (float)atof(v) : 1.5f;
+    }
     a.tree_split = p.tree_split;
     if (p.splits > 1 && p.fill_bytes > 0) {
         const int n = (int)(p.fill_bytes / 4);
