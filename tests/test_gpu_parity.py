@@ -154,9 +154,10 @@ def test_accept_exhaustive_small_trees(jf):
 
 def test_accept_logits_ties_nan_and_alignment(jf):
     rng = np.random.Generator(np.random.PCG64(5))
-    for vocab, dtype in ((5000, torch.bfloat16), (4099, torch.bfloat16), (151936, torch.bfloat16),
-                         (3001, torch.float32), (20000, torch.float32)):
-        B, N = 2, 24
+    # (2, 40, 151936): 200 workgroups per sequence, which arrive in groups
+    for B, N, vocab, dtype in ((2, 24, 5000, torch.bfloat16), (2, 24, 4099, torch.bfloat16),
+                               (2, 24, 151936, torch.bfloat16), (2, 40, 151936, torch.bfloat16),
+                               (2, 24, 3001, torch.float32), (2, 24, 20000, torch.float32)):
         parent = np.stack([W.tree_random_recursive(N, 6, rng) for _ in range(B)])
         z = torch.from_numpy(rng.integers(-3, 4, size=(B, N, vocab)).astype(np.float32)).to(dtype)  # many ties
         z[0, 1] = float("nan")                              # all-NaN row -> 0

@@ -287,8 +287,10 @@ struct AcceptArgs {
     int32_t* accepted_nodes;
     int32_t* bonus;
     int* seq_count;     // [B]       (workspace, zero between calls)
+    int* group_count;   // [B][groups] (workspace, zero between calls; unused when groups == 1)
     uint64_t* partial;  // [B*N*C]   chunk winners as keys (workspace)
     int N, vocab, chunks, chunk_len;
+    int groups;         // arrival groups per sequence (1: every workgroup arrives on seq_count)
     int aligned;        // rows start on 16-byte boundaries and chunk_len keeps them there
 };
 
@@ -315,9 +317,28 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_logits_kernel(AcceptArg
     if (threadIdx.x == 0) {
         __hip_atomic_store(&a.partial[blk], best_key(best), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         wait_own_stores();
-        const int old = arrive(&a.seq_count[b]);
-        last = (old == per_seq - 1);
-        if (last) reset_counter(&a.seq_count[b]);
+        // arrivals in two levels when a sequence has many workgroups: one counter per
+        // group (workgroup index mod groups), then the group's last arriver on the
+        // sequence counter, so no counter sees more than ~per_seq / groups + groups
+        // atomics in a row
+        bool closes = true;
+        int expect = per_seq;
+        if (a.groups > 1) {
+            const int g = (blk - b * per_seq) % a.groups;
+            const int members = (per_seq - g + a.groups - 1) / a.groups;
+            int* gc = a.group_count + b * a.groups + g;
+            const int old = arrive(gc);
+            closes = (old == members - 1);
+            if (closes) reset_counter(gc);
+            expect = a.groups;
+        }
+        int is_last = 0;
+        if (closes) {
+            const int old = arrive(&a.seq_count[b]);
+            is_last = (old == expect - 1);
+            if (is_last) reset_counter(&a.seq_count[b]);
+        }
+        last = is_last;
     }
     __syncthreads();
     if (!last) return;
@@ -355,8 +376,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_logits_kernel(AcceptArg
 // ---------------------------------------------------------------- host side
 
 struct AcceptPlan {
-    int chunks, chunk_len;
-    size_t off_seq, off_part, bytes;
+    int chunks, chunk_len, groups;
+    size_t off_seq, off_group, off_part, bytes;
 };
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -379,6 +400,20 @@ AcceptPlan plan_accept(int B, int N, int vocab) {
     p.chunks = chunks;
     p.chunk_len = len;
     p.off_seq = 0;                                     // B <= kMaxCounters (host check)
+    // two-level arrival for sequences with many workgroups, while the group counters
+    // fit the fixed counter region beside the B sequence counters (every group has
+    // at least one member). Measured: 256 workgroups per sequence 60.8 -> 56.3 us;
+    // at 80 the extra level costs more (9.25 -> 10.05 us) than the contention it saves.
+    const int per_seq = N * chunks;
+    int groups = 1;
+    if (per_seq >= 160 && B > 0) {
+        groups = per_seq / 16 < 16 ? per_seq / 16 : 16;
+        const int room = (kMaxCounters - B) / B;
+        if (groups > room) groups = room;
+        if (groups < 2) groups = 1;
+    }
+    p.groups = groups;
+    p.off_group = (size_t)B * 4;
     p.off_part = kCounterBytes;
     p.bytes = p.off_part + align_up((size_t)rows * chunks * 8, 256);
     return p;
@@ -406,6 +441,8 @@ hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype,
     a.accepted_nodes = accepted_nodes;
     a.bonus = bonus;
     a.seq_count = reinterpret_cast<int*>(ws + p.off_seq);
+    a.group_count = reinterpret_cast<int*>(ws + p.off_group);
+    a.groups = p.groups;
     a.partial = reinterpret_cast<uint64_t*>(ws + p.off_part);
     a.N = N;
     a.vocab = vocab;
