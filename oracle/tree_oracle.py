@@ -281,3 +281,49 @@ def tree_accept(parent, draft, next_tokens):
         a, nd, bo = accept_one(P[b], Dr[b], Nx[b])
         alen[b], nodes[b], bonus[b] = a, nd, bo
     return alen, nodes, bonus
+
+
+def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len, k_pages, v_pages,
+                    page_size: int = 16):
+    """Append each sequence's accepted path to its paged cache.
+
+    After verification the kept tokens become part of the prefix the next
+    step attends to (lay summary: the target keeps the drafted tokens up to
+    its first disagreement; technical summary section 3: that prefix lives in
+    a paged KV cache). Node 0 of a tree is the last committed token, whose K/V
+    was computed together with the tree, so the path's accept_len + 1 nodes
+    are appended: prefix token prefix_len[b] + i receives the K/V of
+    accepted_nodes[b, i], for i = 0 .. accept_len[b].
+
+    A sequence is committed only when prefix_len[b] >= 0, 0 <= accept_len[b]
+    < N, the path entries are node ids in [0, N), and every page its new
+    tokens land in is listed (table slot below the table width, page id in
+    [0, num_pages)); otherwise nothing of it is written and its new length is
+    -1. Arrays are copied element for element (any dtype, bit patterns kept).
+
+    Returns (k_pages', v_pages', new_prefix_len int32[B]).
+    """
+    kt, vt = np.asarray(k_tree), np.asarray(v_tree)
+    kp, vp = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+    alen, nodes = _i64(accept_len), _i64(accepted_nodes)
+    table, plen = _i64(block_table), _i64(prefix_len)
+    B, N = nodes.shape
+    num_pages, width = kp.shape[0], table.shape[1]
+    new_len = np.full(B, -1, dtype=np.int32)
+    for b in range(B):
+        L, a = int(plen[b]), int(alen[b])
+        if L < 0 or not (0 <= a < N):
+            continue
+        path = [int(n) for n in nodes[b, : a + 1]]
+        if any(not (0 <= n < N) for n in path):
+            continue
+        slots = [(L + i) // page_size for i in range(a + 1)]
+        if any(s >= width or not (0 <= int(table[b, s]) < num_pages) for s in slots):
+            continue
+        for i, n in enumerate(path):
+            pos = L + i
+            page = int(table[b, pos // page_size])
+            kp[page, :, pos % page_size, :] = kt[b, n]
+            vp[page, :, pos % page_size, :] = vt[b, n]
+        new_len[b] = L + a + 1
+    return kp, vp, new_len

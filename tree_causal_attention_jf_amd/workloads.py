@@ -195,6 +195,44 @@ def make_paged_kv(prefix_lens, Hkv: int, D: int, dtype: torch.dtype, data_scale:
             k_prefix, v_prefix)
 
 
+@dataclass
+class CommitCase:
+    """Inputs of one commit of accepted paths into a paged cache."""
+    k_pages: torch.Tensor          # [P, Hkv, 16, D]
+    v_pages: torch.Tensor
+    block_table: torch.Tensor      # int32 [B, max_pages]: room for prefix_len[b] + N tokens
+    prefix_len: torch.Tensor       # int32 [B]
+    k_tree: torch.Tensor           # [B, N, Hkv, D]
+    v_tree: torch.Tensor
+    q: torch.Tensor                # [B, N, Hq, D] (for attention-based checks)
+    parent: torch.Tensor           # int32 [B, N]
+    draft: torch.Tensor            # int32 [B, N]
+    target_ids: torch.Tensor       # int32 [B, N]
+
+
+def make_commit_case(seed: int, lens, N: int, Hq: int, Hkv: int, D: int, dtype: torch.dtype = torch.bfloat16,
+                     max_path_nodes: int = 8, p_agree: float = 0.8, extra_pages: int = 3) -> CommitCase:
+    """A paged cache whose block table lists pages for prefix_len[b] + N tokens
+    (the slots past the prefix hold random data, as a reused page would), the
+    tree's own Q/K/V, random recursive draft trees, and draft / target ids for
+    acceptance (ids mode)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = [int(L) for L in lens]
+    scale = 1.0 / math.sqrt(128.0)
+    kp, vp, table, _, _ = make_paged_kv([L + N for L in lens], Hkv, D, dtype, scale, rng, extra_pages=extra_pages)
+    B = len(lens)
+    parent = np.stack([tree_random_recursive(N, max_path_nodes, rng) for _ in range(B)]).astype(np.int32)
+    pairs = [make_accept_ids(parent[b], 1000, p_agree, rng) for b in range(B)]
+    target = np.stack([t for t, _ in pairs])
+    draft = np.stack([d for _, d in pairs])
+    q = _to_dtype(rng.standard_normal((B, N, Hq, D), dtype=np.float32) * scale, dtype)
+    kt = _to_dtype(rng.standard_normal((B, N, Hkv, D), dtype=np.float32) * scale, dtype)
+    vt = _to_dtype(rng.standard_normal((B, N, Hkv, D), dtype=np.float32) * scale, dtype)
+    return CommitCase(kp, vp, table, torch.tensor(lens, dtype=torch.int32), kt, vt, q,
+                      torch.from_numpy(parent), torch.from_numpy(np.asarray(draft, dtype=np.int32)),
+                      torch.from_numpy(np.asarray(target, dtype=np.int32)))
+
+
 def make_accept_ids(parent: np.ndarray, vocab: int, p_agree: float, rng: np.random.Generator):
     """Ids mode: target token per node uniform in [0, vocab); a child's draft
     token equals its parent's target token with probability p_agree, else a
