@@ -204,6 +204,46 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
                          int32_t* bonus_token,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * jf_commit_accepted -- append each sequence's accepted path to its paged KV
+ * cache, the step after acceptance (lay summary: the target keeps the drafted
+ * tokens up to its first disagreement; technical summary, section 3: the
+ * prefix the next step attends to lives in a paged KV cache).
+ *
+ *   s               shape: B, N, Hkv, D, page_size, num_pages,
+ *                   max_pages_per_seq and dtype as for jf_tree_attention
+ *                   (Hq and sm_scale are not used)
+ *   k_tree,v_tree   [B, N, Hkv, D]             K/V of the tree nodes
+ *   accept_len      int32 [B]                  from jf_tree_accept
+ *   accepted_nodes  int32 [B, N]               from jf_tree_accept
+ *   block_table     int32 [B, max_pages_per_seq]
+ *   prefix_len      int32 [B]                  prefix tokens before the call
+ *   k_pages,v_pages [num_pages, Hkv, 16, D]    in/out
+ *   new_prefix_len  int32 [B]                  out: prefix_len[b] + accept_len[b] + 1,
+ *                                              or -1 if sequence b was not committed;
+ *                                              must not overlap prefix_len
+ *
+ * Node 0 is the last committed token, whose K/V was computed with the tree,
+ * so the path's accept_len[b] + 1 nodes are appended: prefix token
+ * prefix_len[b] + i receives the K/V of node accepted_nodes[b, i]. The bonus
+ * token has no K/V yet. A sequence is committed only when prefix_len[b] >= 0,
+ * 0 <= accept_len[b] < N, its path entries are node ids in [0, N), and every
+ * page its new tokens land in is listed (table slot below max_pages_per_seq,
+ * page id in [0, num_pages)); otherwise nothing of it is written and
+ * new_prefix_len[b] = -1. No other page slot is touched. Asynchronous on
+ * `stream`; allocates nothing.
+ *
+ * Host errors: JF_ERR_NULL, JF_ERR_SHAPE (B outside 0..JF_MAX_BATCH, N outside
+ * 1..256, Hkv < 1, negative page counts, new_prefix_len == prefix_len),
+ * JF_ERR_DTYPE, JF_ERR_UNSUPPORTED (D not 64/128, page_size not 16),
+ * JF_ERR_ALIGN (tree K/V or pages not 16-byte aligned), JF_ERR_LAUNCH.
+ */
+jf_status jf_commit_accepted(const jf_attn_shape* s, const void* k_tree, const void* v_tree,
+                             const int32_t* accept_len, const int32_t* accepted_nodes,
+                             const int32_t* block_table, const int32_t* prefix_len,
+                             void* k_pages, void* v_pages, int32_t* new_prefix_len,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,8 @@ def binding():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
-               "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version"):
+               "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
+               "jf_commit_accepted"):
         assert fn in names
 
 
@@ -155,3 +156,40 @@ def test_mask_and_accept_host_checks(binding):
     # logits mode keeps one arrival counter per sequence in the fixed counter region
     big = binding.tree_accept_workspace_bytes(binding.JF_MAX_BATCH + 1, 8, 1000)
     assert acc(B=binding.JF_MAX_BATCH + 1, ws=ctypes.c_void_p(16), wsb=big) == JF_ERR_SHAPE
+
+
+def test_commit_host_checks(binding):
+    L = binding._lib
+    p = ctypes.c_void_p(16)
+
+    def shape(**kw):
+        d = dict(B=2, N=8, Hq=4, Hkv=2, D=128, page_size=16, num_pages=10, max_pages_per_seq=4, dtype=1,
+                 sm_scale=1.0)
+        d.update(kw)
+        return ctypes.byref(binding.AttnShape(**d))
+
+    def commit(s=None, nul=(), align=(), new=None):
+        a = {n: p for n in ("kt", "vt", "alen", "nodes", "table", "plen", "kp", "vp")}
+        a["new"] = ctypes.c_void_p(32) if new is None else new
+        for n in nul:
+            a[n] = None
+        for n in align:
+            a[n] = ctypes.c_void_p(24)
+        return L.jf_commit_accepted(shape() if s is None else s, a["kt"], a["vt"], a["alen"], a["nodes"],
+                                    a["table"], a["plen"], a["kp"], a["vp"], a["new"], None)
+
+    assert L.jf_commit_accepted(None, p, p, p, p, p, p, p, p, p, None) == JF_ERR_NULL
+    assert commit(shape(N=0)) == JF_ERR_SHAPE
+    assert commit(shape(N=257)) == JF_ERR_SHAPE
+    assert commit(shape(B=binding.JF_MAX_BATCH + 1)) == JF_ERR_SHAPE
+    assert commit(shape(Hkv=0)) == JF_ERR_SHAPE
+    assert commit(shape(num_pages=-1)) == JF_ERR_SHAPE
+    assert commit(shape(dtype=7)) == JF_ERR_DTYPE
+    assert commit(shape(D=96)) == JF_ERR_UNSUPPORTED
+    assert commit(shape(page_size=32)) == JF_ERR_UNSUPPORTED
+    for n in ("kt", "vt", "alen", "nodes", "table", "plen", "kp", "vp", "new"):
+        assert commit(nul=(n,)) == JF_ERR_NULL, n
+    for n in ("kt", "vt", "kp", "vp"):
+        assert commit(align=(n,)) == JF_ERR_ALIGN, n
+    assert commit(new=p) == JF_ERR_SHAPE                 # new_prefix_len aliases prefix_len
+    assert commit(shape(B=0)) == JF_OK                   # empty batch: no launch

@@ -33,6 +33,7 @@ EXPORTED = (
     "jf_tree_attention",
     "jf_tree_accept_workspace_bytes",
     "jf_tree_accept",
+    "jf_commit_accepted",
 )
 
 
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_accept_workspace_bytes.argtypes = [i32, i32, i32]
     lib.jf_tree_accept.restype = i32
     lib.jf_tree_accept.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jf_commit_accepted.restype = i32
+    lib.jf_commit_accepted.argtypes = [ctypes.POINTER(AttnShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -253,3 +256,34 @@ def tree_accept(parent, anc, draft, logits: Optional[torch.Tensor] = None,
                              _ptr(bonus_token), _ptr(ws), ws_bytes, _stream(dev))
     _check("jf_tree_accept", st)
     return accept_len, accepted_nodes, bonus_token, next_tokens
+
+
+def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len, k_pages, v_pages,
+                    new_prefix_len: Optional[torch.Tensor] = None):
+    """Append each sequence's accepted path (root included) to its paged cache,
+    in place in k_pages / v_pages (see include/jf_tree.h). Returns
+    new_prefix_len int32 [B] (prefix_len + accept_len + 1, or -1 for a sequence
+    that was not committed)."""
+    for t, n in ((k_tree, "k_tree"), (v_tree, "v_tree"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, k_tree.dtype)
+    for t, n in ((accept_len, "accept_len"), (accepted_nodes, "accepted_nodes"), (block_table, "block_table"),
+                 (prefix_len, "prefix_len")):
+        _need(t, n, torch.int32)
+    B, N, Hkv, D = k_tree.shape
+    P, Hkv_p, page, D_p = k_pages.shape
+    if (Hkv_p, D_p) != (Hkv, D) or tuple(v_pages.shape) != tuple(k_pages.shape) or \
+            tuple(v_tree.shape) != tuple(k_tree.shape):
+        raise ValueError("tree K/V [B, N, Hkv, D] and pages [P, Hkv, 16, D] disagree")
+    dt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}.get(k_tree.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {k_tree.dtype}")
+    shape = AttnShape(B=B, N=N, Hq=Hkv, Hkv=Hkv, D=D, page_size=page, num_pages=P,
+                      max_pages_per_seq=block_table.shape[1], dtype=dt, sm_scale=1.0)
+    dev = k_tree.device
+    if new_prefix_len is None:
+        new_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = _lib.jf_commit_accepted(ctypes.byref(shape), _ptr(k_tree), _ptr(v_tree), _ptr(accept_len),
+                                 _ptr(accepted_nodes), _ptr(block_table), _ptr(prefix_len), _ptr(k_pages),
+                                 _ptr(v_pages), _ptr(new_prefix_len), _stream(dev))
+    _check("jf_commit_accepted", st)
+    return new_prefix_len

@@ -22,6 +22,9 @@ hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype,
                          int32_t* accept_len, int32_t* accepted_nodes, int32_t* bonus, void* workspace,
                          hipStream_t stream);
 size_t accept_workspace_bytes(int B, int N, int vocab);
+hipError_t launch_commit(const jf_attn_shape& s, const void* k_tree, const void* v_tree, const int32_t* accept_len,
+                         const int32_t* accepted_nodes, const int32_t* block_table, const int32_t* prefix_len,
+                         void* k_pages, void* v_pages, int32_t* new_prefix_len, hipStream_t stream);
 }  // namespace jf
 
 namespace {
@@ -135,6 +138,28 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target
     const hipError_t e = jf::launch_accept(B, N, vocab, target_logits, logits_dtype, target_ids, draft_tokens,
                                            parent, anc, next_tokens, accept_len, accepted_nodes, bonus_token,
                                            workspace, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+jf_status jf_commit_accepted(const jf_attn_shape* s, const void* k_tree, const void* v_tree,
+                             const int32_t* accept_len, const int32_t* accepted_nodes, const int32_t* block_table,
+                             const int32_t* prefix_len, void* k_pages, void* v_pages, int32_t* new_prefix_len,
+                             hipStream_t stream) {
+    if (!s) return JF_ERR_NULL;
+    if (s->dtype != JF_F32 && s->dtype != JF_BF16) return JF_ERR_DTYPE;
+    if (s->B < 0 || s->B > JF_MAX_BATCH || s->N < 1 || s->N > JF_MAX_NODES || s->Hkv < 1 || s->num_pages < 0 ||
+        s->max_pages_per_seq < 0)
+        return JF_ERR_SHAPE;
+    if (s->D != 64 && s->D != 128) return JF_ERR_UNSUPPORTED;
+    if (s->page_size != JF_PAGE_SIZE) return JF_ERR_UNSUPPORTED;
+    if (!k_tree || !v_tree || !accept_len || !accepted_nodes || !block_table || !prefix_len || !k_pages || !v_pages ||
+        !new_prefix_len)
+        return JF_ERR_NULL;
+    if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_pages) || !aligned16(v_pages)) return JF_ERR_ALIGN;
+    if (new_prefix_len == prefix_len) return JF_ERR_SHAPE;   // read by every workgroup while one writes
+    if (s->B == 0) return JF_OK;
+    const hipError_t e = jf::launch_commit(*s, k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len,
+                                           k_pages, v_pages, new_prefix_len, stream);
     return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
 }
 
