@@ -260,6 +260,31 @@ def make_steps(jf, wl, sets, with_accept=True):
             [step(s) for s in sets])
 
 
+def time_commit(jf, stream, name, lens, N, Hkv, D, path_nodes):
+    """Average duration of jf_commit_accepted (graph of back-to-back calls) for
+    paths of `path_nodes` nodes; the commit rewrites the same slots each time."""
+    from tree_causal_attention_jf_amd import workloads as W
+    case = W.make_commit_case(0, lens, N=N, Hq=Hkv, Hkv=Hkv, D=D)
+    B = len(lens)
+    alen = torch.full((B,), path_nodes - 1, dtype=torch.int32, device="cuda")
+    nodes = torch.full((B, N), -1, dtype=torch.int32)
+    nodes[:, :path_nodes] = torch.arange(path_nodes, dtype=torch.int32)
+    nodes = nodes.cuda()
+    kt, vt = case.k_tree.cuda(), case.v_tree.cuda()
+    kp, vp = case.k_pages.cuda(), case.v_pages.cuda()
+    table, plen = case.block_table.cuda(), case.prefix_len.cuda()
+    new = torch.empty((B,), dtype=torch.int32, device="cuda")
+    fn = lambda: jf.commit_accepted(kt, vt, alen, nodes, table, plen, kp, vp, new_prefix_len=new)
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    assert new.cpu().tolist() == [L + path_nodes for L in lens]
+    t = time_graph([fn] * 20, 50, stream)
+    moved = 2 * 2 * B * path_nodes * Hkv * D * kt.element_size()      # K and V, read and written
+    return {"workload": name, "us": round(t * 1e3, 3), "bytes": moved,
+            "GBps": round(moved / (t * 1e-3) / 1e9, 1), "bound": "latency"}
+
+
 def rotation_sets(wl, base, budget_bytes=2 * MALL_BYTES, cap=64):
     n = max(1, min(cap, math.ceil(budget_bytes / max(1, base.nbytes()))))
     return [base] + [DeviceSet(wl, src=base) for _ in range(n - 1)]
@@ -483,6 +508,12 @@ def main():
             "input_sets": len(sets4)}
         log(f"[bench] long context: attention {t4 * 1e3:.1f} us ({tf4:.1f} TFLOP/s), accept {tacc4 * 1e3:.1f} us")
         del sets4, b4, a4, acc4, m4
+
+    # ---- commit of accepted paths into the paged cache (the step after acceptance)
+    result["commit"] = [time_commit(jf, stream, *spec) for spec in (
+        ("budget 16: batch 1, 16-node chain fully accepted, 8 KV heads, d=128", [2048], 16, 8, 128, 16),
+        ("budget 256: batch 4, 256-node trees, 12-node accepted paths, 8 KV heads, d=128", [1000] * 4, 256, 8,
+         128, 12))]
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
