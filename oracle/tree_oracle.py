@@ -225,6 +225,44 @@ def tree_attention(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree,
     return out, lse
 
 
+def tree_attention_paged_tree(q, k_pages, v_pages, block_table, prefix_len, tree_len, parent,
+                              sm_scale: Optional[float] = None, page_size: int = 16,
+                              rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Tree-causal attention with ragged budgets and the tree's K/V in the paged cache.
+
+    Sequence b has tree_len[b] = N_b <= N nodes (nodes 0..N_b-1 of q and
+    parent; the rest are padding). Its tree K/V follow its prefix in the
+    cache: node j's key is prefix token L_b + j, so the keys of the sequence are
+    its first L_b + N_b cached tokens, the last N_b of which are the tree's.
+    Otherwise the computation is tree_attention's, for nodes 0..N_b-1 of the
+    tree parent[b, :N_b]. Rows of padding nodes stay NaN.
+    """
+    Q = _f64(q)
+    TL, PL = _i64(tree_len), _i64(prefix_len)
+    BT = _i64(block_table)
+    B, N = Q.shape[0], Q.shape[1]
+    Hq = Q.shape[2]
+    out = np.full(Q.shape, np.nan)
+    lse = np.full(Q.shape[:3], np.nan)
+    want = {}
+    for (b, n, h) in (rows if rows is not None else [(b, n, h) for b in range(B) for n in range(N)
+                                                      for h in range(Hq)]):
+        if int(n) < int(TL[b]):
+            want.setdefault(int(b), []).append((int(n), int(h)))
+    for b, pairs in want.items():
+        L, nb = int(PL[b]), int(TL[b])
+        # the tree's keys and values, gathered from the cache after the prefix
+        kt = gather_prefix(_f64(k_pages), BT[b], L + nb, page_size)[L:][None]
+        vt = gather_prefix(_f64(v_pages), BT[b], L + nb, page_size)[L:][None]
+        o, l = tree_attention(Q[b:b + 1, :nb], k_pages, v_pages, BT[b:b + 1], PL[b:b + 1], kt, vt,
+                              _i64(parent)[b:b + 1, :nb], sm_scale, page_size,
+                              rows=[(0, n, h) for n, h in pairs])
+        for n, h in pairs:
+            out[b, n, h] = o[0, n, h]
+            lse[b, n, h] = l[0, n, h]
+    return out, lse
+
+
 # --------------------------------------------------------------------------
 # Target choice and greedy acceptance (lay summary; qxai.app commentary)
 # --------------------------------------------------------------------------

@@ -410,3 +410,54 @@ def make_workload(name: str, seed: int = 0, *, unscaled: bool = False, poison: b
             wl.draft = torch.from_numpy(np.stack(drafts))
             wl.planted_leaf = torch.tensor(leaves, dtype=torch.int32)
     return wl
+
+
+@dataclass
+class PagedTreeCase:
+    """Ragged tree budgets with each tree's K/V stored in the cache right after
+    its prefix (node j of sequence b is cached token prefix_len[b] + j)."""
+    q: torch.Tensor                # [B, N, Hq, D]; rows of padding nodes are ordinary data
+    k_pages: torch.Tensor          # [P, Hkv, 16, D]: prefix and tree tokens
+    v_pages: torch.Tensor
+    block_table: torch.Tensor      # int32 [B, max_pages]: pages of prefix_len[b] + tree_len[b] tokens
+    prefix_len: torch.Tensor       # int32 [B]
+    tree_len: torch.Tensor         # int32 [B], 0 <= tree_len[b] <= N
+    parent: torch.Tensor           # int32 [B, N]; padding nodes hang under the root
+    draft: torch.Tensor            # int32 [B, N]; -1 for padding nodes
+    k_tree: torch.Tensor           # [B, N, Hkv, D]: the same tree keys as separate arrays (0 for padding)
+    v_tree: torch.Tensor
+    sm_scale: float
+    max_prefix_len: int
+
+
+def make_paged_tree_case(seed: int, lens, budgets, N: int, Hq: int, Hkv: int, D: int, tree=("random", 6),
+                         dtype: torch.dtype = torch.bfloat16, unscaled: bool = False,
+                         extra_pages: int = 2) -> PagedTreeCase:
+    """Sequence b: a prefix of lens[b] tokens followed by its tree's budgets[b]
+    nodes, cached as one contiguous run of tokens in a shuffled page pool.
+    Trees come from the same generators as the workloads (with budgets[b]
+    nodes); padding nodes up to N get parent 0 and draft token -1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = [int(L) for L in lens]
+    budgets = [int(n) for n in budgets]
+    assert len(lens) == len(budgets) and all(0 <= n <= N for n in budgets)
+    scale = 1.0 if unscaled else 1.0 / math.sqrt(128.0)
+    kp, vp, table, kc, vc = make_paged_kv([L + n for L, n in zip(lens, budgets)], Hkv, D, dtype, scale, rng,
+                                          extra_pages=extra_pages)
+    B = len(lens)
+    parent = np.zeros((B, N), dtype=np.int32)
+    draft = np.full((B, N), -1, dtype=np.int32)
+    k_tree = torch.zeros((B, N, Hkv, D), dtype=dtype)
+    v_tree = torch.zeros((B, N, Hkv, D), dtype=dtype)
+    for b, (L, n) in enumerate(zip(lens, budgets)):
+        parent[b, 0] = -1
+        if n > 0:
+            par, _ = make_tree(tree, n, seed, b)
+            parent[b, :n] = par
+            draft[b, 1:n] = rng.integers(0, 1000, size=n - 1)
+            k_tree[b, :n] = kc[b][L:L + n]
+            v_tree[b, :n] = vc[b][L:L + n]
+    q = _to_dtype(rng.standard_normal((B, N, Hq, D), dtype=np.float32) * scale, dtype)
+    return PagedTreeCase(q, kp, vp, table, torch.tensor(lens, dtype=torch.int32),
+                         torch.tensor(budgets, dtype=torch.int32), torch.from_numpy(parent),
+                         torch.from_numpy(draft), k_tree, v_tree, 1.0 / math.sqrt(D), max(lens) if lens else 0)
