@@ -163,6 +163,36 @@ jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * jf_tree_attention_paged_tree -- jf_tree_attention for ragged tree budgets
+ * whose tree K/V are already in the paged cache, right after the prefix (the
+ * verification pass over a paged KV cache, technical summary section 3, with
+ * per-sequence budgets).
+ *
+ * As jf_tree_attention, except:
+ *   - sequence b has tree_len[b] nodes (int32 [B], 0..N; NULL: N for all):
+ *     nodes 0..tree_len[b]-1 of q / anc are its tree, later ones are padding
+ *     and their output rows (and lse) are not written;
+ *   - the K/V of node j is cached token prefix_len[b] + j, so block_table
+ *     must list the pages of prefix_len[b] + tree_len[b] tokens; there are no
+ *     k_tree / v_tree arguments;
+ *   - max_prefix_len bounds prefix_len (the tree's tokens not included);
+ *   - bf16 only (JF_ERR_UNSUPPORTED for fp32).
+ * anc for a padding node must not set bits of real nodes other than 0 (e.g.
+ * parent 0, as jf_build_ancestor_mask gives it); jf_tree_accept never accepts
+ * a padding node whose draft token is -1. A tree_len[b] outside [0, N], or a
+ * tree page that is not listed, sets every row of sequence b to NaN. Same
+ * workspace (jf_tree_attention_workspace_bytes) and host errors as
+ * jf_tree_attention, plus JF_ERR_SHAPE when num_pages or max_pages_per_seq
+ * is 0.
+ */
+jf_status jf_tree_attention_paged_tree(const jf_attn_shape* s, int32_t max_prefix_len,
+                                       const void* q, const void* k_pages, const void* v_pages,
+                                       const int32_t* block_table, const int32_t* prefix_len,
+                                       const int32_t* tree_len, const uint64_t* anc,
+                                       void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of workspace jf_tree_accept needs in logits mode (ids mode needs
  * none). Same workspace contract as jf_tree_attention: the two entry points
  * may share one workspace.

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
-               "jf_commit_accepted"):
+               "jf_commit_accepted", "jf_tree_attention_paged_tree"):
         assert fn in names
 
 
@@ -193,3 +193,35 @@ def test_commit_host_checks(binding):
         assert commit(align=(n,)) == JF_ERR_ALIGN, n
     assert commit(new=p) == JF_ERR_SHAPE                 # new_prefix_len aliases prefix_len
     assert commit(shape(B=0)) == JF_OK                   # empty batch: no launch
+
+
+def test_paged_tree_attention_host_checks(binding):
+    L = binding._lib
+    p = ctypes.c_void_p(16)
+
+    def shape(**kw):
+        d = dict(B=2, N=8, Hq=4, Hkv=2, D=128, page_size=16, num_pages=10, max_pages_per_seq=4, dtype=1,
+                 sm_scale=0.1)
+        d.update(kw)
+        return binding.AttnShape(**d)
+
+    def call(s=None, maxp=20, nul=(), align=(), ws=None, wsb=0):
+        a = {n: p for n in ("q", "kp", "vp", "table", "plen", "anc", "out")}
+        for n in nul:
+            a[n] = None
+        for n in align:
+            a[n] = ctypes.c_void_p(24)
+        return L.jf_tree_attention_paged_tree(ctypes.byref(shape() if s is None else s), maxp, a["q"], a["kp"],
+                                              a["vp"], a["table"], a["plen"], None, a["anc"], a["out"], None, ws,
+                                              wsb, None)
+
+    assert call(shape(dtype=0)) == JF_ERR_UNSUPPORTED              # bf16 only
+    assert call(shape(D=96)) == JF_ERR_UNSUPPORTED
+    assert call(shape(N=0)) == JF_ERR_SHAPE
+    assert call(maxp=65) == JF_ERR_SHAPE                           # beyond the block table
+    assert call(shape(num_pages=0), maxp=0) == JF_ERR_SHAPE         # the tree itself must be cached
+    for n in ("q", "kp", "vp", "table", "plen", "anc", "out"):
+        assert call(nul=(n,)) == JF_ERR_NULL, n
+    for n in ("q", "kp", "vp", "out"):
+        assert call(align=(n,)) == JF_ERR_ALIGN, n
+    assert call(shape(B=0)) == JF_OK

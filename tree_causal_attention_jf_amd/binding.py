@@ -34,6 +34,7 @@ EXPORTED = (
     "jf_tree_accept_workspace_bytes",
     "jf_tree_accept",
     "jf_commit_accepted",
+    "jf_tree_attention_paged_tree",
 )
 
 
@@ -80,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_accept_workspace_bytes.argtypes = [i32, i32, i32]
     lib.jf_tree_accept.restype = i32
     lib.jf_tree_accept.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jf_tree_attention_paged_tree.restype = i32
+    lib.jf_tree_attention_paged_tree.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, sz, vp]
     lib.jf_commit_accepted.restype = i32
     lib.jf_commit_accepted.argtypes = [ctypes.POINTER(AttnShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     return lib
@@ -210,6 +214,38 @@ def tree_attention(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree,
                                 _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc),
                                 _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev))
     _check("jf_tree_attention", st)
+    return (out, lse) if return_lse else out
+
+
+def tree_attention_paged_tree(q, k_pages, v_pages, block_table, prefix_len, anc, tree_len=None,
+                              sm_scale: Optional[float] = None, max_prefix_len: Optional[int] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Tree-causal attention with ragged budgets, the tree's K/V cached right after
+    each prefix (see include/jf_tree.h). Rows of padding nodes are left as they are
+    in `out` (allocate it yourself to control them)."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, q.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(prefix_len, "prefix_len", torch.int32)
+    _need(anc, "anc", torch.uint64)
+    if tree_len is not None:
+        _need(tree_len, "tree_len", torch.int32)
+    shape = attn_shape(q, k_pages, block_table, sm_scale)
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_len.max().item()) if prefix_len.numel() else 0
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    need = tree_attention_workspace_bytes(shape, max_prefix_len)
+    ws = workspace if workspace is not None else _default_ws.get(dev, "attn", need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib.jf_tree_attention_paged_tree(ctypes.byref(shape), int(max_prefix_len), _ptr(q), _ptr(k_pages),
+                                           _ptr(v_pages), _ptr(block_table), _ptr(prefix_len), _ptr(tree_len),
+                                           _ptr(anc), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev))
+    _check("jf_tree_attention_paged_tree", st)
     return (out, lse) if return_lse else out
 
 

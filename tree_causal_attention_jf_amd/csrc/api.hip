@@ -11,7 +11,8 @@ hipError_t launch_ancestor_mask(const int32_t* parent, int B, int N, uint64_t* a
 hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
                                  const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
                                  const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
-                                 float* lse, void* workspace, hipStream_t stream);
+                                 float* lse, void* workspace, hipStream_t stream, const int32_t* tree_len = nullptr,
+                                 int paged_tree = 0);
 hipError_t launch_attention_f32(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
                                 const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
                                 const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
@@ -110,6 +111,28 @@ jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len, cons
     else
         e = jf::launch_attention_f32(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree,
                                      v_tree, anc, out, lse, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+jf_status jf_tree_attention_paged_tree(const jf_attn_shape* s, int32_t max_prefix_len, const void* q,
+                                       const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                       const int32_t* prefix_len, const int32_t* tree_len, const uint64_t* anc,
+                                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    const jf_status st = check_attn_shape(s, max_prefix_len);
+    if (st != JF_OK) return st;
+    if (s->dtype != JF_BF16) return JF_ERR_UNSUPPORTED;
+    if (!q || !k_pages || !v_pages || !block_table || !prefix_len || !anc || !out) return JF_ERR_NULL;
+    if (s->num_pages < 1 || s->max_pages_per_seq < 1) return JF_ERR_SHAPE;   // the tree itself is cached
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(out)) return JF_ERR_ALIGN;
+    const size_t need = jf_tree_attention_workspace_bytes(s, max_prefix_len);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return JF_ERR_ALIGN;
+    }
+    if (s->B == 0) return JF_OK;
+    const hipError_t e = jf::launch_attention_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,
+                                                   nullptr, nullptr, anc, out, lse, workspace, stream, tree_len, 1);
     return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
 }
 

@@ -59,6 +59,7 @@ constexpr int kKeyTile = 64;
 constexpr int kRing = 4;                 // LDS tile buffers
 constexpr int kMaxPagesPerSplit = 1024;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxTreePages = JF_MAX_NODES / 16 + 1;   // pages a paged tree of up to 256 nodes spans
 constexpr int kMaxBalanced = 64;         // batches planned from their prefix lengths inside the kernel (one wave)
 
 struct AttnArgs {
@@ -86,6 +87,8 @@ struct AttnArgs {
     int cus;           // compute units of the device (ditto)
     int forced;        // balanced: every sequence takes `splits` pieces (tuning and tests)
     float cut;         // balanced: a sequence is cut when its work exceeds cut x the mean per CU
+    const int32_t* tree_len;  // [B] nodes of each tree (NULL: all N); rows of later nodes are not written
+    int paged_tree;    // 1: node j's K/V is cached token prefix_len[b] + j (kt / vt unused)
     int tree_split;    // 1: split splits-1 runs the tree tiles alone, the others the prefix
     float scale_log2;  // sm_scale * log2(e)
 };
@@ -191,7 +194,8 @@ template <int D, int CNT, typename SrcFn>
 __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* vp, const uint16_t* kt,
                                             const uint16_t* vt, int N, int Hkv, SrcFn tile_src, int round_first_tile,
                                             int n_tiles, int b, int kvh, const int* s_pages,
-                                            const PageLanes<D>& pl, uint32_t buf, int first, int lane) {
+                                            const PageLanes<D>& pl, uint32_t buf, int first, int lane,
+                                            const int* s_tp, int tok0) {
     using Gm = Geo<D>;
     constexpr int TPP = PageLanes<D>::TPP;
     static_assert(CNT % TPP == 0, "a wave moves whole pages");
@@ -221,8 +225,15 @@ __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* 
                 const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
                 const uint16_t* gp;
                 if (src.tree) {
-                    const int t = min(src.t0 + row, src.limit - 1);
-                    gp = (isv ? vt : kt) + (((long)b * N + t) * Hkv + kvh) * D + c * 8;
+                    const int t = min(src.t0 + row, src.limit - 1);    // nodes past the tree: its last node
+                    if (tok0 >= 0) {
+                        // paged tree: node t is cached token tok0 + t; s_tp lists the pages from tok0's on
+                        const int tok = tok0 + t;
+                        const int page = s_tp[(tok >> 4) - (tok0 >> 4)];
+                        gp = (isv ? vp : kp) + (((long)page * Hkv + kvh) * kPage + (tok & 15)) * D + c * 8;
+                    } else {
+                        gp = (isv ? vt : kt) + (((long)b * N + t) * Hkv + kvh) * D + c * 8;
+                    }
                 } else {
                     int t = src.t0 + row;
                     if (t >= src.limit) t = src.t0;
@@ -454,7 +465,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     __shared__ unsigned long long s_union[kAncWords];
     __shared__ int s_last;
     __shared__ int s_plan[4];
-    __shared__ int s_epi[5];
+    __shared__ int s_epi[6];
+    __shared__ int s_tpages[kMaxTreePages];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave index: uniform
@@ -549,6 +561,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     const int p_begin = tree_wg ? 0 : s * pps;
     const int p_avail = tree_wg ? 0 : min(pps, a.max_pages - p_begin);
     int L = a.prefix_len[b];
+    int nb = a.tree_len ? a.tree_len[b] : a.N;
     int pid[PPT];
     #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -573,12 +586,18 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         #pragma unroll
         for (int c = 0; c < DCH; ++c) qreg[blk][c] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * c));
     }
-    #pragma unroll
-    for (int blk = 0; blk < RPW; ++blk)
-        if (!row_ok[blk]) ancw[blk] = u64x4{0, 0, 0, 0};
-
     bool bad = (L < 0 || L > a.max_prefix);
     if (bad) L = 0;
+    if (nb < 0 || nb > a.N) {                       // a bad tree length: every row of the sequence is NaN
+        bad = true;
+        nb = a.N;
+    }
+    // rows of nodes past the tree's length are not computed into the output
+    #pragma unroll
+    for (int blk = 0; blk < RPW; ++blk) {
+        row_ok[blk] = row_ok[blk] && node[blk] < nb;
+        if (!row_ok[blk]) ancw[blk] = u64x4{0, 0, 0, 0};
+    }
     const int npages = (L + kPage - 1) / kPage;
     // splits that hold work: the prefix splits, and the tree either in the last of
     // them or (tree_split) in its own slot, splits - 1
@@ -624,6 +643,19 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         }
     }
     int my_bad = 0;
+    // paged tree: the pages holding cached tokens L .. L + nb - 1 (at most kMaxTreePages)
+    if (a.paged_tree && has_tree && nb > 0) {
+        const int first = L / kPage, count = (L + nb - 1) / kPage - first + 1;
+        if (tid < count) {
+            const int slot = first + tid;
+            int v = slot < a.max_pages ? a.block_table[(long)b * a.max_pages + slot] : -1;
+            if (v < 0 || v >= a.num_pages) {
+                my_bad = 1;
+                v = 0;
+            }
+            s_tpages[tid] = v;
+        }
+    }
     #pragma unroll
     for (int k = 0; k < PPT; ++k) {
         const int i = tid + k * T;
@@ -644,6 +676,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         s_epi[2] = rb;
         s_epi[3] = n_act;
         s_epi[4] = n_pre_splits;
+        s_epi[5] = nb;
     }
     bad = __syncthreads_or(my_bad) || bad;
 
@@ -670,12 +703,13 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         } else {
             src.tree = true;
             src.t0 = ((tree_list >> (2 * (it - n_pre))) & 3) * kKeyTile;
-            src.limit = N;
+            src.limit = nb;
         }
         return src;
     };
 
     const uint32_t ring0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)ring);
+    const int tree_tok0 = a.paged_tree ? L : -1;      // paged tree: cached token of node 0
     const uint16_t* const g_kp = a.kp;
     const uint16_t* const g_vp = a.vp;
     const uint16_t* const g_kt = a.kt;
@@ -719,7 +753,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         for (int p = 0; p < RING_R - 1; ++p)
             if (p < n_rounds)
                 issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, p * KW, n_tiles, b, kvh, s_pages, pl,
-                                    ring0 + p * KW * Gm::BUF_BYTES, w * DPR, lane);
+                                    ring0 + p * KW * Gm::BUF_BYTES, w * DPR, lane, s_tpages, tree_tok0);
     }
     // (a one-round ring issues each round and waits for all of it, which also covers
     // the set-up loads still landing from before its first round)
@@ -729,10 +763,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
             __syncthreads();      // round r is in LDS for every wave; the buffers of round r-1 are free
             if (r + RING_R - 1 < n_rounds)
                 issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, (r + RING_R - 1) * KW, n_tiles, b, kvh, s_pages, pl,
-                                    ring0 + ((r + RING_R - 1) % RING_R) * KW * Gm::BUF_BYTES, w * DPR, lane);
+                                    ring0 + ((r + RING_R - 1) % RING_R) * KW * Gm::BUF_BYTES, w * DPR, lane,
+                                    s_tpages, tree_tok0);
         } else {
             __syncthreads();      // every wave is done with the previous round
-            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl, ring0, w * DPR, lane);
+            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl, ring0,
+                                w * DPR, lane, s_tpages, tree_tok0);
             wait_vm<0>();
             __syncthreads();
         }
@@ -749,6 +785,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     rb = __builtin_amdgcn_readfirstlane(s_epi[2]);
     n_act = __builtin_amdgcn_readfirstlane(s_epi[3]);
     const int n_pre_e = __builtin_amdgcn_readfirstlane(s_epi[4]);
+    const int nb_e = __builtin_amdgcn_readfirstlane(s_epi[5]);
     const float NANF = __builtin_nanf("");
     const float LN2 = 0.69314718055994530942f;
     float* mo = reinterpret_cast<float*>(ring);      // key-group merge area (reuses the ring)
@@ -846,7 +883,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                                                                   merge_off<D>(rl, c * TPR + part));
         }
         if (n_act == 1) {
-            if (grow < a.rows) {
+            if (grow < a.rows && grow / a.G < nb_e) {
                 const int gnode = grow / a.G, ghead = kvh * a.G + grow % a.G;
                 const float inv = bad ? NANF : 1.f / Ls;
                 uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * 4;
@@ -899,7 +936,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         const uint32_t base = (uint32_t)item * a.splits * RB;        // + slot * RB
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
-        const bool out_ok = grow < a.rows;
+        const bool out_ok = grow < a.rows && grow / a.G < nb_e;
         const int gnode = out_ok ? grow / a.G : 0, ghead = kvh * a.G + (out_ok ? grow % a.G : 0);
         // the thread's CPT chunks in passes of CB; per pass, one batch of loads (every
         // split's m, l and O slice) per SB splits, merged with a running max so no
@@ -1089,7 +1126,8 @@ static hipError_t launch_bf16_d(const AttnPlanBf16& p, const AttnArgs& a, hipStr
 hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
                                  const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
                                  const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
-                                 float* lse, void* workspace, hipStream_t stream) {
+                                 float* lse, void* workspace, hipStream_t stream, const int32_t* tree_len,
+                                 int paged_tree) {
     const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
     if (p.grid == 0) return hipSuccess;
     AttnArgs a;
@@ -1130,6 +1168,8 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
         a.cut = (v && *v) ? (float)atof(v) : 1.5f;
     }
     a.tree_split = p.tree_split;
+    a.tree_len = tree_len;
+    a.paged_tree = paged_tree;
     if (p.splits > 1 && p.fill_bytes > 0) {
         const int n = (int)(p.fill_bytes / 4);
         hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream,
