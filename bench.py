@@ -285,6 +285,43 @@ def time_commit(jf, stream, name, lens, N, Hkv, D, path_nodes):
             "GBps": round(moved / (t * 1e-3) / 1e9, 1), "bound": "latency"}
 
 
+def time_paged_tree(jf, stream, seed=0):
+    """Ragged budgets with the trees' K/V cached after their prefixes: batch 8,
+    best-first trees with budgets U{16..256} (N = 256), prefixes U[1024, 4096],
+    32q/8kv, d = 128. Returns the JSON entry."""
+    from tree_causal_attention_jf_amd import workloads as W
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(1024, 4097, size=8).tolist()
+    budgets = rng.integers(16, 257, size=8).tolist()
+    case = W.make_paged_tree_case(seed, lens, budgets, N=256, Hq=32, Hkv=8, D=128, tree=("best_first", 4, 12, 2.0))
+    t = {k: getattr(case, k).cuda() for k in ("q", "k_pages", "v_pages", "block_table", "prefix_len", "tree_len",
+                                               "parent")}
+    anc, depth, _ = jf.build_ancestor_mask(t["parent"])
+    out = torch.empty_like(t["q"])
+    fn = lambda: jf.tree_attention_paged_tree(t["q"], t["k_pages"], t["v_pages"], t["block_table"],
+                                              t["prefix_len"], anc, tree_len=t["tree_len"], sm_scale=case.sm_scale,
+                                              max_prefix_len=case.max_prefix_len, out=out)
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    ms = time_graph([fn] * 10, 20, stream)
+    # algorithmic work of the real nodes only: prefix keys plus ancestors, per query head
+    dep = depth.cpu().numpy().astype(np.int64)
+    L = np.asarray(lens, dtype=np.int64)
+    pairs = sum(int((L[b] + dep[b, :budgets[b]]).sum()) for b in range(8))
+    flops = 4 * 128 * 32 * pairs
+    nodes = int(sum(budgets))
+    nbytes = int((L.sum() + nodes) * 8 * 128 * 2 * 2 + 2 * nodes * 32 * 128 * 2 + nodes * 32 +
+                 ((L + np.asarray(budgets) + 15) // 16).sum() * 4)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"batch 8, best-first trees of budgets {budgets} (N 256), prefixes {lens}, tree K/V "
+                        "cached after each prefix, 32q/8kv, d=128",
+            "attention_us": round(ms * 1e3, 3), "tree_tokens_per_s": round(nodes / (ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops,
+                         "algorithmic_bytes": nbytes}}
+
+
 def rotation_sets(wl, base, budget_bytes=2 * MALL_BYTES, cap=64):
     n = max(1, min(cap, math.ceil(budget_bytes / max(1, base.nbytes()))))
     return [base] + [DeviceSet(wl, src=base) for _ in range(n - 1)]
@@ -508,6 +545,12 @@ def main():
             "input_sets": len(sets4)}
         log(f"[bench] long context: attention {t4 * 1e3:.1f} us ({tf4:.1f} TFLOP/s), accept {tacc4 * 1e3:.1f} us")
         del sets4, b4, a4, acc4, m4
+
+    # ---- ragged budgets with the trees' K/V in the paged cache
+    if not args.no_budget256:
+        result["ragged_budgets"] = time_paged_tree(jf, stream)
+        log(f"[bench] ragged budgets: {result['ragged_budgets']['attention_us']} us, "
+            f"{result['ragged_budgets']['roofline']['achieved']} TFLOP/s")
 
     # ---- commit of accepted paths into the paged cache (the step after acceptance)
     result["commit"] = [time_commit(jf, stream, *spec) for spec in (

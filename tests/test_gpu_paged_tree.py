@@ -88,6 +88,17 @@ def test_paged_tree_forced_plans(jf, rw, splits, balanced, monkeypatch):
     _check(case, out, lse, what=f"rw {rw} splits {splits} balanced {balanced}")
 
 
+@pytest.mark.parametrize("balanced", [1, 0])
+def test_paged_tree_row_blocks_past_the_budget(jf, balanced, monkeypatch):
+    # N 256 at G 4 gives four 256-row blocks per KV head; budgets 3, 0 and 70 leave
+    # whole blocks without a node of the tree (they exit), 256 leaves none
+    monkeypatch.setenv("JF_BALANCED", str(balanced))
+    case = W.make_paged_tree_case(29, [40, 300, 17, 129], [3, 0, 70, 256], N=256, Hq=8, Hkv=2, D=128,
+                                  tree=("random", 11))
+    out, lse = _run(jf, case)
+    _check(case, out, lse, what=f"balanced {balanced}")
+
+
 def test_full_budgets_match_the_separate_tree_kernel_bit_for_bit(jf):
     case = W.make_paged_tree_case(25, [300, 17, 64], [24, 24, 24], N=24, Hq=8, Hkv=2, D=128, tree=("random", 6))
     out, lse = _run(jf, case)

@@ -474,10 +474,12 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     // ---- which (sequence, KV head, split, row block) this workgroup owns
     int rb, s, kvh, b, pps;
     if (a.balanced) {
-        // Balanced schedule, planned alike by every workgroup from the prefix lengths:
-        //  * a sequence whose work (prefix tiles + tree tiles) exceeds 1.5x the mean
-        //    work per CU is cut into ceil(work / mean) pieces (at most `splits`) of
-        //    equal page counts;
+        // Balanced schedule, planned alike by every workgroup from the prefix (and
+        // tree) lengths:
+        //  * a sequence whose work per workgroup (prefix tiles + tree tiles) exceeds
+        //    1.5x the mean work per CU is cut into ceil(work / mean) pieces (at most
+        //    `splits`) of equal page counts; the mean counts only row blocks that
+        //    hold rows of the tree (the others exit at once);
         //  * units (sequence, piece, KV head) are ranked by piece size, largest first,
         //    and dealt round robin to the XCDs; a unit's nrb row blocks (which read
         //    the same K/V pages) run one after another on one XCD.
@@ -485,15 +487,19 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         // list-schedules its own longest-first share. Ids past the units are idle.
         if (w == 0) {
             const int Lm = lane < a.B ? a.prefix_len[lane] : 0;
+            int nbm = (a.tree_len && lane < a.B) ? a.tree_len[lane] : a.N;
+            if (nbm < 0 || nbm > a.N) nbm = a.N;       // a bad length computes every row (as NaN)
             const int pg = (lane < a.B && Lm > 0 && Lm <= a.max_prefix) ? (Lm + kPage - 1) / kPage : 0;
-            const int tiles = (pg + 3) / 4 + a.tree_tiles;
-            int tot = lane < a.B ? tiles : 0;
+            const int tiles = (pg + 3) / 4 + min(a.tree_tiles, (nbm + kKeyTile - 1) / kKeyTile);
+            const int live = min(a.nrb, (nbm * a.G + RB - 1) / RB);        // row blocks with rows
+            int tot = lane < a.B ? tiles * live : 0;
             #pragma unroll
             for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-            const float mean = (float)tot * (float)(a.Hkv * a.nrb) / (float)a.cus;
+            const float mean = (float)tot * (float)a.Hkv / (float)a.cus;
             int n = 1;
             if (a.forced) n = a.splits;
-            else if (mean > 0.f && (float)tiles > a.cut * mean) n = min(a.splits, (int)ceilf((float)tiles / mean));
+            else if (mean > 0.f && live > 0 && (float)tiles > a.cut * mean)
+                n = min(a.splits, (int)ceilf((float)tiles / mean));
             n = min(n, max(1, pg / (4 * KW)));                            // a full round of tiles per piece
             n = max(n, (pg + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);  // (the host keeps this <= splits)
             int pp = (pg + n - 1) / n;
@@ -592,6 +598,7 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         bad = true;
         nb = a.N;
     }
+    if (rb * RB >= nb * a.G) return;                // uniform: no row of the block is a node of the tree
     // rows of nodes past the tree's length are not computed into the output
     #pragma unroll
     for (int blk = 0; blk < RPW; ++blk) {
