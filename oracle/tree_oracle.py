@@ -29,7 +29,10 @@ Everything the pages leave open is resolved by the plainest reading:
     agrees, ties to the smallest end-node index; the bonus token is the
     target's choice at the end of that path;
   - the target's choice at a node is the first index of the largest logit;
-    NaN never wins; a row of NaN only yields 0.
+    NaN never wins; a row of NaN only yields 0;
+  - tree construction: row i of the draft logits belongs to the i-th node to
+    join the tree; candidates are ordered by cumulative log-probability, then
+    by their parent's join order, then by rank (logit, then token id).
 
 Arithmetic is fp64 throughout. Inputs stored in bf16 or fp32 are widened
 exactly, so the oracle sees the same rounded values the GPU sees.
@@ -37,6 +40,7 @@ exactly, so the oracle sees the same rounded values the GPU sees.
 
 from __future__ import annotations
 
+import heapq
 import math
 from typing import Iterable, Optional, Sequence, Tuple
 
@@ -365,3 +369,91 @@ def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, pre
             vp[page, :, pos % page_size, :] = vt[b, n]
         new_len[b] = L + a + 1
     return kp, vp, new_len
+
+
+# --------------------------------------------------------------------------
+# Best-first tree construction (technical summaries, section 2, "tree
+# construction": the draft head emits logits for the whole tree in one pass;
+# nodes are ranked by their cumulative draft log-probability, and a best-first
+# expansion grows the candidate tree to the token budget)
+# --------------------------------------------------------------------------
+
+def draft_children(row, topk: int):
+    """The children a node offers: its topk most likely next tokens.
+
+    row is the node's draft logits over the vocabulary. NaN entries count as
+    -inf. The log-probability of token t is row[t] - logsumexp(row). Tokens
+    are ranked by logit, larger first, ties to the smaller token id; tokens of
+    -inf logit are never offered, and a row whose largest entry is not finite
+    (only -inf / NaN, or any +inf) offers nothing.
+
+    Returns (tokens int list, log-probabilities float list), best first."""
+    z = _f64(row).reshape(-1).copy()
+    z[np.isnan(z)] = -np.inf
+    m = z.max()
+    if not np.isfinite(m):
+        return [], []
+    lse = m + math.log(float(np.exp(z - m).sum()))
+    finite = np.nonzero(z > -np.inf)[0]
+    k = min(topk, finite.size)
+    # the k-th largest logit bounds the candidates; rank those by (-logit, token)
+    kth = np.partition(z[finite], finite.size - k)[finite.size - k]
+    cand = finite[z[finite] >= kth]
+    cand = cand[np.lexsort((cand, -z[cand]))][:k]
+    return [int(t) for t in cand], [float(z[t] - lse) for t in cand]
+
+
+def build_tree(draft_logits, topk: int, max_path_nodes: int, budget=None):
+    """Best-first construction of one draft tree per sequence.
+
+    draft_logits [B, N, V]: row i of sequence b is the draft head's output at
+    the tree's node i, nodes being numbered in the order they join the tree
+    (node 0 is the root, the last committed token). Node i's children are
+    draft_children(row i, topk), each scored by the node's cumulative log-
+    probability plus the child's log-probability. The candidate with the best
+    score joins next, ties to the candidate whose parent joined first, then to
+    the better-ranked child; it becomes the next node and, unless its root-to-
+    node path already holds max_path_nodes nodes, offers its own children.
+    Growth stops at budget[b] nodes (None: N) or when no candidate is left.
+
+    Returns (parent int32[B, N], token int32[B, N], score float64[B, N],
+    tree_len int32[B]). Node 0 has parent -1 and token -1 (score 0). Nodes at
+    or past tree_len[b] are padding: parent 0 (node 0 keeps -1 when the budget
+    is 0), token -1, score -inf.
+    """
+    X = _f64(draft_logits)
+    B, N, _ = X.shape
+    nb_all = [N] * B if budget is None else [int(x) for x in _i64(budget).reshape(-1)]
+    parent = np.zeros((B, N), dtype=np.int32)
+    parent[:, 0] = -1
+    token = np.full((B, N), -1, dtype=np.int32)
+    score = np.full((B, N), -np.inf)
+    tree_len = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        nb = nb_all[b]
+        if not 0 <= nb <= N:
+            raise ValueError(f"sequence {b}: budget {nb} outside [0, {N}]")
+        if nb == 0:
+            continue
+        score[b, 0] = 0.0
+        depth = [1]
+        heap: list = []
+
+        def offer(v: int) -> None:
+            if depth[v] >= max_path_nodes:
+                return
+            toks, lps = draft_children(X[b, v], topk)
+            for r, (t, lp) in enumerate(zip(toks, lps)):
+                heapq.heappush(heap, (-(score[b, v] + lp), v, r, t))
+
+        offer(0)
+        n = 1
+        while n < nb and heap:
+            neg, v, _, t = heapq.heappop(heap)
+            parent[b, n], token[b, n], score[b, n] = v, t, -neg
+            depth.append(depth[v] + 1)
+            n += 1
+            if n < nb:
+                offer(n - 1)
+        tree_len[b] = n
+    return parent, token, score, tree_len

@@ -461,3 +461,43 @@ def make_paged_tree_case(seed: int, lens, budgets, N: int, Hq: int, Hkv: int, D:
     return PagedTreeCase(q, kp, vp, table, torch.tensor(lens, dtype=torch.int32),
                          torch.tensor(budgets, dtype=torch.int32), torch.from_numpy(parent),
                          torch.from_numpy(draft), k_tree, v_tree, 1.0 / math.sqrt(D), max(lens) if lens else 0)
+
+
+# --------------------------------------------------------------------------
+# Draft logits for best-first tree construction
+# --------------------------------------------------------------------------
+
+@dataclass
+class DraftLogitsCase:
+    logits: torch.Tensor           # [B, N, V]: row i = the draft head's output at the i-th node to join
+    topk: int
+    max_path_nodes: int
+    budget: torch.Tensor           # int32 [B], 0 <= budget[b] <= N
+
+
+def make_draft_logits_case(seed: int, B: int, N: int, vocab: int, topk: int = 4, max_path_nodes: int = 12,
+                           sigma: float = 2.0, budgets=None, dtype: torch.dtype = torch.bfloat16,
+                           kind: str = "normal") -> DraftLogitsCase:
+    """Draft logits i.i.d. N(0, sigma^2) over the vocabulary (the draft-logit
+    recipe of the budget-256 workloads), rounded to dtype. Other kinds:
+      "uniform"     all-zero rows;
+      "ties"        normal rows in which topk + 2 random positions are raised to
+                    the row's largest value, so the best logits of a row tie;
+      "small_ints"  integers 0..3, so equal logits are common inside and
+                    across rows.
+    budgets: per-sequence node budgets (None: N)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if kind in ("normal", "ties"):
+        z = rng.standard_normal((B, N, vocab), dtype=np.float32) * np.float32(sigma)
+        if kind == "ties":
+            z = _to_dtype(z, dtype).float().numpy()
+            for row in z.reshape(-1, vocab):
+                row[rng.choice(vocab, size=min(vocab, topk + 2), replace=False)] = row.max()
+    elif kind == "uniform":
+        z = np.zeros((B, N, vocab), dtype=np.float32)
+    elif kind == "small_ints":
+        z = rng.integers(0, 4, size=(B, N, vocab)).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    bud = [N] * B if budgets is None else [int(x) for x in budgets]
+    return DraftLogitsCase(_to_dtype(z, dtype), topk, max_path_nodes, torch.tensor(bud, dtype=torch.int32))
