@@ -63,6 +63,8 @@ enum { JF_F32 = 0, JF_BF16 = 1 };
 /* Most sequences one jf_tree_attention call takes (its work schedule is
  * formed on the device from all B prefix lengths). */
 #define JF_MAX_BATCH 1024
+/* children a node may offer in jf_build_tree */
+#define JF_MAX_TOPK 8
 /* Size of the counter region at the start of every workspace (see the
  * workspace notes of jf_tree_attention and jf_tree_accept). */
 #define JF_WORKSPACE_COUNTER_BYTES 4096
@@ -273,6 +275,50 @@ jf_status jf_commit_accepted(const jf_attn_shape* s, const void* k_tree, const v
                              const int32_t* block_table, const int32_t* prefix_len,
                              void* k_pages, void* v_pages, int32_t* new_prefix_len,
                              hipStream_t stream);
+
+
+/*
+ * jf_build_tree -- best-first construction of the draft tree (technical
+ * summaries, section 2, tree construction: the draft head emits logits for
+ * the whole tree in one pass, nodes are ranked by cumulative draft
+ * log-probability, and a best-first expansion grows the tree to the budget).
+ *
+ *   draft_logits    [B, N, vocab] of logits_dtype (JF_BF16 or JF_F32). Row i
+ *                   of sequence b is the draft head's output at the i-th node
+ *                   to join the tree (node 0: the root, the last committed
+ *                   token). Rows at or past budget[b] - 1 are never read.
+ *   topk            1..JF_MAX_TOPK children offered per node: its topk most
+ *                   likely tokens, larger logit first, ties to the smaller id
+ *   max_path_nodes  >= 1; a node whose root-to-node path holds this many nodes
+ *                   offers no children
+ *   budget          int32 [B] nodes per tree, or NULL (N for every sequence)
+ *   parent, token   int32 [B, N] out: the tree in join order. Node 0 has parent
+ *                   -1 and token -1. Nodes at or past tree_len[b] are padding:
+ *                   parent 0, token -1 (as jf_tree_attention_paged_tree and
+ *                   jf_tree_accept expect them)
+ *   score           float64 [B, N] out, nullable: each node's cumulative draft
+ *                   log-probability (root 0, padding -inf)
+ *   tree_len        int32 [B] out: nodes grown, at most budget[b]; fewer when no
+ *                   candidate is left; -1 for a budget outside [0, N]
+ *
+ * A child's log-probability is its logit minus the row's logsumexp, in fp64.
+ * NaN logits count as -inf; tokens of -inf logit are never offered; a row
+ * whose largest entry is not finite offers nothing. The best candidate joins
+ * next: larger score first, then the candidate whose parent joined first, then
+ * the better-ranked child. Workspace: jf_build_tree_workspace_bytes, same
+ * contract as jf_tree_attention (may be shared with the other entry points,
+ * not between calls in flight at once). Asynchronous on `stream`.
+ *
+ * Host errors: JF_ERR_NULL, JF_ERR_SHAPE (B outside 0..JF_MAX_BATCH, N outside
+ * 1..256, vocab < 1, topk outside 1..JF_MAX_TOPK, max_path_nodes < 1),
+ * JF_ERR_DTYPE, JF_ERR_WORKSPACE, JF_ERR_ALIGN (workspace not 16-byte
+ * aligned), JF_ERR_LAUNCH.
+ */
+size_t jf_build_tree_workspace_bytes(int32_t B, int32_t N, int32_t vocab, int32_t topk, int32_t logits_dtype);
+jf_status jf_build_tree(int32_t B, int32_t N, int32_t vocab, const void* draft_logits, int32_t logits_dtype,
+                        int32_t topk, int32_t max_path_nodes, const int32_t* budget,
+                        int32_t* parent, int32_t* token, double* score, int32_t* tree_len,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

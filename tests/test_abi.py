@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
-               "jf_commit_accepted", "jf_tree_attention_paged_tree"):
+               "jf_commit_accepted", "jf_tree_attention_paged_tree", "jf_build_tree",
+               "jf_build_tree_workspace_bytes"):
         assert fn in names
 
 
@@ -51,7 +52,7 @@ def test_every_declared_symbol_is_exported(binding):
 def test_header_limits_match_the_binding(binding):
     text = open(HEADER).read()
     for name, value in (("JF_MAX_NODES", binding.MAX_NODES), ("JF_PAGE_SIZE", binding.PAGE_SIZE),
-                        ("JF_MAX_BATCH", binding.JF_MAX_BATCH),
+                        ("JF_MAX_BATCH", binding.JF_MAX_BATCH), ("JF_MAX_TOPK", binding.JF_MAX_TOPK),
                         ("JF_WORKSPACE_COUNTER_BYTES", binding.JF_WORKSPACE_COUNTER_BYTES)):
         assert re.search(r"#define %s (\d+)" % name, text).group(1) == str(value), name
 
@@ -225,3 +226,36 @@ def test_paged_tree_attention_host_checks(binding):
     for n in ("q", "kp", "vp", "out"):
         assert call(align=(n,)) == JF_ERR_ALIGN, n
     assert call(shape(B=0)) == JF_OK
+
+
+def test_build_tree_host_checks(binding):
+    L = binding._lib
+    p = ctypes.c_void_p(16)
+    need = L.jf_build_tree_workspace_bytes(2, 16, 1000, 4, 1)
+    assert need >= binding.JF_WORKSPACE_COUNTER_BYTES
+    assert L.jf_build_tree_workspace_bytes(2, 16, 1000, 9, 1) == 0            # topk beyond the limit
+    assert L.jf_build_tree_workspace_bytes(2, 16, 1000, 4, 5) == 0            # unknown dtype
+
+    def call(B=2, N=16, V=1000, dt=1, k=4, cap=6, nul=(), ws=None, wsb=None):
+        a = {n: p for n in ("logits", "parent", "token", "len")}
+        for n in nul:
+            a[n] = None
+        w = ctypes.c_void_p(4096) if ws is None else ws
+        return L.jf_build_tree(B, N, V, a["logits"], dt, k, cap, None, a["parent"], a["token"], None, a["len"],
+                               w, need if wsb is None else wsb, None)
+
+    assert call(N=0) == JF_ERR_SHAPE
+    assert call(N=257) == JF_ERR_SHAPE
+    assert call(B=-1) == JF_ERR_SHAPE
+    assert call(B=binding.JF_MAX_BATCH + 1) == JF_ERR_SHAPE
+    assert call(V=0) == JF_ERR_SHAPE
+    assert call(k=0) == JF_ERR_SHAPE
+    assert call(k=binding.JF_MAX_TOPK + 1) == JF_ERR_SHAPE
+    assert call(cap=0) == JF_ERR_SHAPE
+    assert call(dt=3) == JF_ERR_DTYPE
+    for n in ("logits", "parent", "token", "len"):
+        assert call(nul=(n,)) == JF_ERR_NULL, n
+    assert call(wsb=need - 1) == JF_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0)) == JF_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(4104)) == JF_ERR_ALIGN
+    assert call(B=0) == JF_OK                                                  # empty batch: no launch

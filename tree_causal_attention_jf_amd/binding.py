@@ -23,6 +23,7 @@ JF_F32, JF_BF16 = 0, 1
 MAX_NODES = 256
 PAGE_SIZE = 16
 JF_MAX_BATCH = 1024          # sequences per tree_attention call (include/jf_tree.h)
+JF_MAX_TOPK = 8              # children per node in build_tree
 JF_WORKSPACE_COUNTER_BYTES = 4096   # counter region at the start of every workspace
 
 EXPORTED = (
@@ -35,6 +36,8 @@ EXPORTED = (
     "jf_tree_accept",
     "jf_commit_accepted",
     "jf_tree_attention_paged_tree",
+    "jf_build_tree_workspace_bytes",
+    "jf_build_tree",
 )
 
 
@@ -86,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  vp, vp, sz, vp]
     lib.jf_commit_accepted.restype = i32
     lib.jf_commit_accepted.argtypes = [ctypes.POINTER(AttnShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.jf_build_tree_workspace_bytes.restype = sz
+    lib.jf_build_tree_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.jf_build_tree.restype = i32
+    lib.jf_build_tree.argtypes = [i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     return lib
 
 
@@ -323,3 +330,39 @@ def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, pre
                                  _ptr(v_pages), _ptr(new_prefix_len), _stream(dev))
     _check("jf_commit_accepted", st)
     return new_prefix_len
+
+
+def build_tree_workspace_bytes(B: int, N: int, vocab: int, topk: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(_lib.jf_build_tree_workspace_bytes(B, N, vocab, topk,
+                                                  {torch.bfloat16: JF_BF16, torch.float32: JF_F32}[dtype]))
+
+
+def build_tree(draft_logits, topk: int, max_path_nodes: int, budget: Optional[torch.Tensor] = None,
+               parent=None, token=None, score=None, tree_len=None, return_score: bool = True,
+               workspace: Optional[torch.Tensor] = None):
+    """Best-first draft tree from draft logits [B, N, V] (bf16/fp32), row i being
+    the draft head's output at the i-th node to join. Returns (parent int32 [B, N],
+    token int32 [B, N], score float64 [B, N] or None, tree_len int32 [B])."""
+    _need(draft_logits, "draft_logits")
+    dt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}.get(draft_logits.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {draft_logits.dtype}")
+    B, N, V = draft_logits.shape
+    dev = draft_logits.device
+    if budget is not None:
+        _need(budget, "budget", torch.int32, (B,))
+    if parent is None:
+        parent = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if token is None:
+        token = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if score is None and return_score:
+        score = torch.empty((B, N), dtype=torch.float64, device=dev)
+    if tree_len is None:
+        tree_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = int(_lib.jf_build_tree_workspace_bytes(B, N, V, topk, dt))
+    ws = workspace if workspace is not None else _default_ws.get(dev, "build", max(need, 1))
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = _lib.jf_build_tree(B, N, V, _ptr(draft_logits), dt, topk, max_path_nodes, _ptr(budget), _ptr(parent),
+                            _ptr(token), _ptr(score), _ptr(tree_len), _ptr(ws), ws_bytes, _stream(dev))
+    _check("jf_build_tree", st)
+    return parent, token, score, tree_len

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libjf_tree.so")
-SOURCES = ["api.hip", "mask.hip", "accept.hip", "attn_bf16.hip", "attn_f32.hip", "commit.hip"]
+SOURCES = ["api.hip", "mask.hip", "accept.hip", "attn_bf16.hip", "attn_f32.hip", "commit.hip", "tree_build.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions stay off: the compiler must not form v_pk_{add,mul,fma}_f32.

@@ -26,6 +26,10 @@ size_t accept_workspace_bytes(int B, int N, int vocab);
 hipError_t launch_commit(const jf_attn_shape& s, const void* k_tree, const void* v_tree, const int32_t* accept_len,
                          const int32_t* accepted_nodes, const int32_t* block_table, const int32_t* prefix_len,
                          void* k_pages, void* v_pages, int32_t* new_prefix_len, hipStream_t stream);
+size_t build_workspace_bytes(int B, int N, int vocab, int topk, int dtype);
+hipError_t launch_build(int B, int N, int vocab, const void* logits, int dtype, int topk, int cap,
+                        const int32_t* budget, int32_t* parent, int32_t* token, double* score, int32_t* tree_len,
+                        void* workspace, hipStream_t stream);
 }  // namespace jf
 
 namespace {
@@ -183,6 +187,35 @@ jf_status jf_commit_accepted(const jf_attn_shape* s, const void* k_tree, const v
     if (s->B == 0) return JF_OK;
     const hipError_t e = jf::launch_commit(*s, k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len,
                                            k_pages, v_pages, new_prefix_len, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+namespace {
+bool build_shape_ok(int32_t B, int32_t N, int32_t vocab, int32_t topk) {
+    return B >= 0 && B <= JF_MAX_BATCH && B <= JF_WORKSPACE_COUNTER_BYTES / 4 && N >= 1 && N <= JF_MAX_NODES &&
+           vocab >= 1 && topk >= 1 && topk <= JF_MAX_TOPK &&
+           (long)B * (N > 1 ? N - 1 : 1) * ((vocab + 16383) / 16384) <= 0x7fffffffL;
+}
+}  // namespace
+
+size_t jf_build_tree_workspace_bytes(int32_t B, int32_t N, int32_t vocab, int32_t topk, int32_t logits_dtype) {
+    if (!build_shape_ok(B, N, vocab, topk) || (logits_dtype != JF_F32 && logits_dtype != JF_BF16)) return 0;
+    return jf::build_workspace_bytes(B, N, vocab, topk, logits_dtype);
+}
+
+jf_status jf_build_tree(int32_t B, int32_t N, int32_t vocab, const void* draft_logits, int32_t logits_dtype,
+                        int32_t topk, int32_t max_path_nodes, const int32_t* budget, int32_t* parent,
+                        int32_t* token, double* score, int32_t* tree_len, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    if (!build_shape_ok(B, N, vocab, topk) || max_path_nodes < 1) return JF_ERR_SHAPE;
+    if (logits_dtype != JF_F32 && logits_dtype != JF_BF16) return JF_ERR_DTYPE;
+    if (!draft_logits || !parent || !token || !tree_len) return JF_ERR_NULL;
+    const size_t need = jf::build_workspace_bytes(B, N, vocab, topk, logits_dtype);
+    if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return JF_ERR_ALIGN;
+    if (B == 0) return JF_OK;
+    const hipError_t e = jf::launch_build(B, N, vocab, draft_logits, logits_dtype, topk, max_path_nodes, budget,
+                                          parent, token, score, tree_len, workspace, stream);
     return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
 }
 

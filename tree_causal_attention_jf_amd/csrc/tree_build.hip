@@ -1,0 +1,606 @@
+// Best-first construction of the draft tree from the draft head's logits.
+//
+// What is computed (technical summaries of "JetFlow ...", section 2, tree
+// construction): the draft head emits a logits row for every node of the tree
+// in one pass; a node offers its topk most likely next tokens as children,
+// each scored by the node's cumulative draft log-probability plus the child's
+// log-probability; a best-first expansion adds the best-scored candidate next
+// until the token budget is reached. Row i of a sequence belongs to the i-th
+// node to join (node 0 is the root, the last committed token). Readings:
+//   * log p(t) = z_t - logsumexp(z), in fp64; NaN logits count as -inf,
+//     tokens of -inf logit are never offered, a row whose largest entry is not
+//     finite offers nothing;
+//   * ranks inside a row: larger logit first, then the smaller token id;
+//   * candidates: larger score first, then the parent that joined first, then
+//     the better rank; a node whose root-to-node path holds max_path_nodes
+//     nodes is not expanded; growth stops at the budget or when nothing is left.
+//
+// One launch:
+//  1. workgroup (sequence b, row i, chunk c) streams one 32768-value chunk
+//     (16384 for fp32) of row i with 16-byte loads held in registers, and
+//     computes the chunk's largest logit m_c, s_c = sum exp(z - m_c) in fp64,
+//     and its topk keys (value, then smaller index); it publishes them with
+//     agent-scope atomic stores and arrives on the sequence's counter (two
+//     levels when the sequence has many workgroups). Only rows that can be
+//     expanded run: i < budget - 1.
+//  2. the sequence's last workgroup merges each row's chunks (logsumexp and
+//     topk), then one wave grows the tree: each selected node keeps one head
+//     (its best child not yet taken) in the registers of lane node % 64; each
+//     step takes the best head across the wave (DPP max of the fp64 scores,
+//     ties to the smaller parent id), appends it as the next node, advances
+//     its parent's head and gives the new node its first head.
+// The arrival counters return to zero, so the workspace never needs clearing
+// again (the same counter region as the other entry points).
+#include "jf_common.h"
+
+namespace jf {
+
+constexpr int kBuildThreads = 256;
+constexpr int kBuildVecs = 16;       // 16-byte vectors per thread per chunk (held in registers)
+
+struct BuildArgs {
+    const void* logits;         // [B, N, vocab]
+    const int32_t* budget;      // [B] or NULL (N)
+    int32_t* parent;            // [B, N]
+    int32_t* token;             // [B, N]
+    double* score;              // [B, N] or NULL
+    int32_t* tree_len;          // [B]
+    int* seq_count;             // [B]            workspace, zero between calls
+    int* group_count;           // [B][groups]    workspace, zero between calls
+    unsigned long long* rec;    // [B][N-1][chunks][rec_words] chunk records (workspace)
+    int N, vocab, chunks, chunk_len, topk, cap, groups, rec_words, aligned;
+};
+
+// ---------------------------------------------------------------- keys
+
+// Order-preserving unsigned image of a float (-0 read as +0).
+__device__ __forceinline__ uint32_t ord32(float v) {
+    uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Chunk-local keys: larger = larger value, then smaller index; 0 = no entry.
+// bf16 values keep their 16 significant bits, so value and a 16-bit index fit
+// one 32-bit key; fp32 values need 64 bits.
+template <typename T> struct KeyOf;
+template <> struct KeyOf<uint16_t> {
+    using type = uint32_t;
+    __device__ static __forceinline__ type make(float v, int local) {
+        return ((ord32(v) >> 16) << 16) | (uint32_t)(0xffff - local);
+    }
+    __device__ static __forceinline__ float value(type k) {
+        const uint32_t o = k >> 16;                            // order image of the bf16 bits
+        const uint32_t h = (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);
+        return __uint_as_float(h << 16);
+    }
+    __device__ static __forceinline__ int index(type k) { return 0xffff - (int)(k & 0xffffu); }
+};
+template <> struct KeyOf<float> {
+    using type = unsigned long long;
+    __device__ static __forceinline__ type make(float v, int local) {
+        return ((type)ord32(v) << 32) | (type)(0xffffffffu - (uint32_t)local);
+    }
+    __device__ static __forceinline__ float value(type k) { return unord32((uint32_t)(k >> 32)); }
+    __device__ static __forceinline__ int index(type k) { return (int)(0xffffffffu - (uint32_t)k); }
+};
+
+template <typename K, int KT>
+__device__ __forceinline__ void insert_sorted(K (&l)[KT], K x) {
+    #pragma unroll
+    for (int j = 0; j < KT; ++j) {
+        const K hi = l[j] > x ? l[j] : x;
+        x = l[j] > x ? x : l[j];
+        l[j] = hi;
+    }
+}
+
+// ---------------------------------------------------------------- wave reductions (DPP inside rows of 16)
+
+constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double maxd(double a, double b) { return a > b ? a : b; }
+
+// Largest value of the wave (no NaN among the inputs), the same in every lane.
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = maxd(v, dpp_f64<kDppQuad1032>(v));
+    v = maxd(v, dpp_f64<kDppQuad2301>(v));
+    v = maxd(v, dpp_f64<kDppRowHalfMirror>(v));
+    v = maxd(v, dpp_f64<kDppRowMirror>(v));
+    return maxd(maxd(readlane_f64(v, 0), readlane_f64(v, 16)), maxd(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t minu(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = minu(v, dpp32<kDppQuad1032>(v));
+    v = minu(v, dpp32<kDppQuad2301>(v));
+    v = minu(v, dpp32<kDppRowHalfMirror>(v));
+    v = minu(v, dpp32<kDppRowMirror>(v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return minu(minu(a, b), minu(c, d));
+}
+
+template <typename K>
+__device__ __forceinline__ K wave_max_key(K v) {
+    #pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        K w;
+        if constexpr (sizeof(K) == 4) {
+            w = (K)__shfl_xor((int)v, o);
+        } else {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+            w = ((K)hi << 32) | lo;
+        }
+        v = v > w ? v : w;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- phase 2: the tree
+
+// Writes sequence b's tree: parent / token / score for every node, tree_len.
+// s_lp / s_tok / s_cnt hold each expandable row's children (rows < rows_live).
+// Run by wave 0 alone.
+template <int KT>
+__device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
+                          const int* s_cnt) {
+    const int lane = threadIdx.x;
+    const int N = a.N;
+    int32_t* par = a.parent + (size_t)b * N;
+    int32_t* tok = a.token + (size_t)b * N;
+    double* sc = a.score ? a.score + (size_t)b * N : nullptr;
+    const double ninf = -__builtin_inf();
+
+    // slot s of lane l is node s * 64 + l: its score, depth, child count, next rank,
+    // head value (its best child not yet taken, -inf: none) and the head's successor
+    double hs[4], hv[4], hn[4];
+    int hd[4], hc[4], hr[4];
+    #pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int v = s * 64 + lane;
+        hs[s] = 0.0;
+        hv[s] = ninf;
+        hn[s] = ninf;
+        hd[s] = 0;
+        hr[s] = 0;
+        hc[s] = (v < rows_live) ? s_cnt[v] : 0;
+    }
+    int n = 0;
+    if (nb >= 1) {
+        if (lane == 0) {
+            par[0] = -1;
+            tok[0] = -1;
+            if (sc) sc[0] = 0.0;
+            hd[0] = 1;
+            if (1 < a.cap && hc[0] > 0) {
+                hv[0] = s_lp[0];
+                hn[0] = hc[0] > 1 ? s_lp[1] : ninf;
+            }
+        }
+        n = 1;
+    }
+    while (n < nb) {
+        // best head of this lane: larger value, ties to the smaller slot (smaller node id)
+        double bv = hv[0];
+        int bs = 0;
+        #pragma unroll
+        for (int s = 1; s < 4; ++s) {
+            if (hv[s] > bv) {
+                bv = hv[s];
+                bs = s;
+            }
+        }
+        const double wv = wave_max_f64(bv);
+        if (!(wv > ninf)) break;                                   // no candidate left (uniform)
+        const unsigned long long tied = __ballot(bv == wv);
+        int wp;                                                    // parent of the new node
+        if (__builtin_popcountll(tied) == 1) {
+            const int owner = __builtin_ctzll(tied);
+            wp = __builtin_amdgcn_readlane(bs, owner) * 64 + owner;
+        } else {
+            wp = (int)wave_min_u32(bv == wv ? (uint32_t)(bs * 64 + lane) : 0xffffffffu);
+        }
+        wp = __builtin_amdgcn_readfirstlane(wp);
+        const int owner = wp & 63, slot = wp >> 6;
+        // the owner takes the head: the new node's token, depth; its next child becomes the head
+        int nd = 0;
+        if (lane == owner) {
+            #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s == slot) {
+                    const int r = hr[s];
+                    tok[n] = s_tok[wp * KT + r];
+                    par[n] = wp;
+                    if (sc) sc[n] = wv;
+                    nd = hd[s] + 1;
+                    hr[s] = r + 1;
+                    hv[s] = (r + 1 < hc[s]) ? hs[s] + hn[s] : ninf;
+                    hn[s] = (r + 2 < hc[s]) ? s_lp[wp * KT + r + 2] : ninf;
+                }
+            }
+        }
+        nd = __builtin_amdgcn_readlane(nd, owner);
+        // the new node's first head
+        if (lane == (n & 63)) {
+            const int ns = n >> 6;
+            #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s == ns) {
+                    hs[s] = wv;
+                    hd[s] = nd;
+                    hr[s] = 0;
+                    if (nd < a.cap && hc[s] > 0) {                // hc = 0 for rows past rows_live
+                        hv[s] = wv + s_lp[n * KT];
+                        hn[s] = hc[s] > 1 ? s_lp[n * KT + 1] : ninf;
+                    }
+                }
+            }
+        }
+        ++n;
+    }
+    // padding
+    for (int v = (n > 1 ? n : 1) + lane; v < N; v += 64) {
+        par[v] = 0;
+        tok[v] = -1;
+    }
+    if (sc)
+        for (int v = n + lane; v < N; v += 64) sc[v] = ninf;
+    if (nb < 1 && lane == 0) {
+        par[0] = -1;
+        tok[0] = -1;
+    }
+    if (lane == 0) a.tree_len[b] = (nb >= 0 && nb <= N) ? n : -1;
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <typename T, int KT>
+__global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
+    using KO = KeyOf<T>;
+    using K = typename KO::type;
+    constexpr int EPV = 16 / (int)sizeof(T);                 // elements per 16-byte vector
+    constexpr int kNW = kBuildThreads / kWave;
+    __shared__ __attribute__((aligned(16))) double s_lp[JF_MAX_NODES * KT];   // phase 1 reuses it for keys
+    __shared__ int s_tok[JF_MAX_NODES * KT];
+    __shared__ int s_cnt[JF_MAX_NODES];
+    __shared__ float s_m[kNW];
+    __shared__ double s_s[kNW];
+    __shared__ int s_last;
+    static_assert(sizeof(K) * kBuildThreads * KT <= sizeof(double) * JF_MAX_NODES * KT, "key scratch");
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int R = a.N > 1 ? a.N - 1 : 1;
+    const int blk = blockIdx.x;
+    const int c = blk % a.chunks;
+    const int i = (blk / a.chunks) % R;
+    const int b = blk / (a.chunks * R);
+    const int nb = a.budget ? a.budget[b] : a.N;
+    const bool nb_ok = nb >= 0 && nb <= a.N;
+    const int rows_live = (nb_ok && a.cap > 1 && nb >= 2) ? nb - 1 : 0;
+
+    if (rows_live == 0) {
+        // nothing to expand: the first workgroup of the sequence writes its tree
+        if (i == 0 && c == 0 && w == 0) grow_tree<KT>(a, b, nb_ok ? nb : -1, 0, s_lp, s_tok, s_cnt);
+        return;
+    }
+    if (i >= rows_live) return;
+
+    // ---- phase 1: one chunk of row i, four 16-byte vectors per thread at a time
+    // with the next four in flight. Per value: its key into this thread's sorted
+    // top-KT, and exp(z - M_t) into an fp64 sum, where the reference M_t moves up
+    // only when a value exceeds it by more than 512 (then the sum is rescaled), so
+    // no term overflows and no separate max pass is needed.
+    const T* rp = reinterpret_cast<const T*>(a.logits) + ((size_t)b * a.N + i) * a.vocab;
+    const int lo = c * a.chunk_len;
+    const int hi = min(a.vocab, lo + a.chunk_len);
+    constexpr int G = 4;                                        // vectors per group
+    auto load_group = [&](int g, u32x4 (&dst)[G]) {
+        #pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int v = g * G + q;
+            const int e0 = (v * kBuildThreads + t) * EPV;       // chunk-local index of the vector
+            if (a.aligned) {
+                const u32x4* vp = reinterpret_cast<const u32x4*>(rp + lo);
+                dst[q] = (lo + e0 < hi) ? __builtin_nontemporal_load(vp + v * kBuildThreads + t) : u32x4{0, 0, 0, 0};
+            } else {
+                uint32_t wd[4] = {0, 0, 0, 0};
+                #pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const int idx = lo + e0 + e;
+                    uint32_t x = 0;
+                    if (idx < hi) {
+                        if constexpr (sizeof(T) == 2) x = (uint32_t)reinterpret_cast<const uint16_t*>(rp)[idx];
+                        else x = __float_as_uint(reinterpret_cast<const float*>(rp)[idx]);
+                    }
+                    if constexpr (sizeof(T) == 2) wd[e >> 1] |= x << (16 * (e & 1));
+                    else wd[e] = x;
+                }
+                dst[q] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            }
+        }
+    };
+    K top[KT];
+    #pragma unroll
+    for (int j = 0; j < KT; ++j) top[j] = 0;
+    float M_t = -__builtin_inff();
+    double s_t = 0.0;
+    u32x4 cur[G], nxt[G];
+    load_group(0, cur);
+    #pragma unroll 1
+    for (int g = 0; g < kBuildVecs / G; ++g) {
+        if (g + 1 < kBuildVecs / G) load_group(g + 1, nxt);
+        #pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int v = g * G + q;
+            float z[EPV];
+            bool ok[EPV];
+            float vmax = -__builtin_inff();
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                if constexpr (sizeof(T) == 2) z[e] = __uint_as_float((cur[q][e >> 1] >> (16 * (e & 1))) << 16);
+                else z[e] = __uint_as_float(cur[q][e]);
+                const int local = (v * kBuildThreads + t) * EPV + e;
+                ok[e] = (lo + local < hi) && z[e] > -__builtin_inff();   // NaN and -inf never enter
+                insert_sorted<K, KT>(top, ok[e] ? KO::make(z[e], local) : (K)0);
+                vmax = ok[e] ? fmaxf(vmax, z[e]) : vmax;
+            }
+            if (vmax > M_t + 512.f) {                           // first values, or a far larger one
+                if (M_t > -__builtin_inff()) s_t *= exp((double)M_t - (double)vmax);
+                M_t = vmax;
+            }
+            const double md = (double)M_t;
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) s_t += ok[e] ? exp((double)z[e] - md) : 0.0;
+        }
+        #pragma unroll
+        for (int q = 0; q < G; ++q) cur[q] = nxt[q];
+    }
+    // this thread's largest value
+    const float m_t = top[0] ? KO::value(top[0]) : -__builtin_inff();
+    // chunk max, then the chunk's sum rescaled to it
+    float m_w = m_t;
+    #pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m_w = fmaxf(m_w, __shfl_xor(m_w, o));
+    K* s_keys = reinterpret_cast<K*>(s_lp);
+    #pragma unroll
+    for (int j = 0; j < KT; ++j) s_keys[t * KT + j] = top[j];
+    if (lane == 0) s_m[w] = m_w;
+    __syncthreads();
+    float m_c = s_m[0];
+    #pragma unroll
+    for (int k = 1; k < kNW; ++k) m_c = fmaxf(m_c, s_m[k]);
+    double part = (M_t > -__builtin_inff() && s_t > 0.0) ? s_t * exp((double)M_t - (double)m_c) : 0.0;
+    #pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long u = (unsigned long long)__double_as_longlong(part);
+        const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)u, o), phi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), o);
+        part += __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
+    }
+    if (lane == 0) s_s[w] = part;
+    __syncthreads();
+    if (w == 0) {
+        // merge the 256 threads' lists: lane l takes threads 4l .. 4l+3, then KT rounds
+        // of the wave's largest head
+        K mine[KT];
+        #pragma unroll
+        for (int j = 0; j < KT; ++j) mine[j] = 0;
+        #pragma unroll
+        for (int q = 0; q < 4; ++q)
+            #pragma unroll
+            for (int j = 0; j < KT; ++j) insert_sorted<K, KT>(mine, s_keys[(lane * 4 + q) * KT + j]);
+        unsigned long long* rec =
+            a.rec + (((size_t)b * (a.N > 1 ? a.N - 1 : 1) + i) * a.chunks + c) * (size_t)a.rec_words;
+        for (int r = 0; r < KT; ++r) {
+            const K best = wave_max_key<K>(mine[0]);
+            if (lane == 0) {
+                unsigned long long word;
+                if (best) word = ((unsigned long long)(uint32_t)(lo + KO::index(best)) << 32) |
+                                 __float_as_uint(KO::value(best));
+                else word = (0xffffffffull << 32) | __float_as_uint(-__builtin_inff());
+                __hip_atomic_store(rec + 2 + r, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (best && mine[0] == best) {              // keys are distinct: one lane pops
+                #pragma unroll
+                for (int j = 0; j + 1 < KT; ++j) mine[j] = mine[j + 1];
+                mine[KT - 1] = 0;
+            }
+        }
+        if (lane == 0) {
+            double s_c = s_s[0];
+            #pragma unroll
+            for (int k = 1; k < kNW; ++k) s_c += s_s[k];
+            __hip_atomic_store(rec + 0, (unsigned long long)__float_as_uint(m_c), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(rec + 1, (unsigned long long)__double_as_longlong(s_c), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            wait_own_stores();
+            // arrival (two levels when the sequence has many workgroups)
+            const int per_seq = rows_live * a.chunks;
+            bool closes = true;
+            int expect = per_seq;
+            if (a.groups > 1) {
+                const int g = (i * a.chunks + c) % a.groups;
+                const int members = (per_seq - g + a.groups - 1) / a.groups;
+                int* gc = a.group_count + b * a.groups + g;
+                const int old = arrive(gc);
+                closes = (old == members - 1);
+                if (closes) reset_counter(gc);
+                expect = per_seq < a.groups ? per_seq : a.groups;
+            }
+            int is_last = 0;
+            if (closes) {
+                const int old = arrive(&a.seq_count[b]);
+                is_last = (old == expect - 1);
+                if (is_last) reset_counter(&a.seq_count[b]);
+            }
+            s_last = is_last;
+        }
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // ---- phase 2 (the sequence's last workgroup): each row's logsumexp and children
+    const unsigned long long* rb = a.rec + (size_t)b * (a.N > 1 ? a.N - 1 : 1) * a.chunks * a.rec_words;
+    if (t < rows_live) {
+        const unsigned long long* rr = rb + (size_t)t * a.chunks * a.rec_words;
+        float m = -__builtin_inff();
+        for (int cc = 0; cc < a.chunks; ++cc) {
+            const unsigned long long w0 =
+                __hip_atomic_load(rr + (size_t)cc * a.rec_words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            m = fmaxf(m, __uint_as_float((uint32_t)w0));
+        }
+        int cnt = 0;
+        if (m > -__builtin_inff() && m < __builtin_inff()) {
+            double s = 0.0;
+            unsigned long long best[KT];
+            #pragma unroll
+            for (int j = 0; j < KT; ++j) best[j] = 0;
+            for (int cc = 0; cc < a.chunks; ++cc) {
+                const unsigned long long* rc = rr + (size_t)cc * a.rec_words;
+                const float mc = __uint_as_float((uint32_t)__hip_atomic_load(rc, __ATOMIC_RELAXED,
+                                                                             __HIP_MEMORY_SCOPE_AGENT));
+                const double scc = __longlong_as_double((long long)__hip_atomic_load(rc + 1, __ATOMIC_RELAXED,
+                                                                                     __HIP_MEMORY_SCOPE_AGENT));
+                if (mc > -__builtin_inff()) s += scc * exp((double)mc - (double)m);
+                #pragma unroll
+                for (int j = 0; j < KT; ++j) {
+                    const unsigned long long e = __hip_atomic_load(rc + 2 + j, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    const float ev = __uint_as_float((uint32_t)e);
+                    const uint32_t etok = (uint32_t)(e >> 32);
+                    // global key: value, then the smaller token id
+                    const unsigned long long key = ev > -__builtin_inff()
+                                                       ? (((unsigned long long)ord32(ev) << 32) | (0xffffffffu - etok))
+                                                       : 0ull;
+                    insert_sorted<unsigned long long, KT>(best, key);
+                }
+            }
+            const double lse = (double)m + log(s);
+            #pragma unroll
+            for (int j = 0; j < KT; ++j) {
+                if (j < a.topk && best[j]) {
+                    s_lp[t * KT + j] = (double)unord32((uint32_t)(best[j] >> 32)) - lse;
+                    s_tok[t * KT + j] = (int)(0xffffffffu - (uint32_t)best[j]);
+                    cnt = j + 1;
+                }
+            }
+        }
+        s_cnt[t] = cnt;
+    }
+    __syncthreads();
+    if (w == 0) grow_tree<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt);
+}
+
+// ---------------------------------------------------------------- host side
+
+struct BuildPlan {
+    int chunks, chunk_len, groups, rec_words, kt;
+    size_t off_group, off_rec, bytes;
+};
+
+static size_t align_up_b(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+BuildPlan plan_build(int B, int N, int vocab, int topk, int dtype) {
+    BuildPlan p{};
+    p.kt = topk <= 1 ? 1 : topk <= 2 ? 2 : topk <= 4 ? 4 : 8;
+    const int epv = dtype == JF_BF16 ? 8 : 4;
+    p.chunk_len = kBuildThreads * kBuildVecs * epv;          // 32768 bf16 / 16384 fp32 values
+    p.chunks = (vocab + p.chunk_len - 1) / p.chunk_len;
+    p.rec_words = 2 + p.kt;
+    const int R = N > 1 ? N - 1 : 1;
+    const int per_seq = R * p.chunks;
+    int groups = 1;
+    if (per_seq >= 160 && B > 0) {
+        groups = per_seq / 16 < 16 ? per_seq / 16 : 16;
+        const int room = (kMaxCounters - B) / B;
+        if (groups > room) groups = room;
+        if (groups < 2) groups = 1;
+    }
+    p.groups = groups;
+    p.off_group = (size_t)B * 4;
+    p.off_rec = kCounterBytes;
+    p.bytes = p.off_rec + align_up_b((size_t)B * R * p.chunks * p.rec_words * 8, 256);
+    return p;
+}
+
+size_t build_workspace_bytes(int B, int N, int vocab, int topk, int dtype) {
+    return plan_build(B, N, vocab, topk, dtype).bytes;
+}
+
+template <typename T, int KT>
+static void launch_build_t(const BuildArgs& a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((tree_build_kernel<T, KT>), dim3(grid), dim3(kBuildThreads), 0, stream, a);
+}
+
+hipError_t launch_build(int B, int N, int vocab, const void* logits, int dtype, int topk, int cap,
+                        const int32_t* budget, int32_t* parent, int32_t* token, double* score, int32_t* tree_len,
+                        void* workspace, hipStream_t stream) {
+    const BuildPlan p = plan_build(B, N, vocab, topk, dtype);
+    char* ws = static_cast<char*>(workspace);
+    BuildArgs a{};
+    a.logits = logits;
+    a.budget = budget;
+    a.parent = parent;
+    a.token = token;
+    a.score = score;
+    a.tree_len = tree_len;
+    a.seq_count = reinterpret_cast<int*>(ws);
+    a.group_count = reinterpret_cast<int*>(ws + p.off_group);
+    a.rec = reinterpret_cast<unsigned long long*>(ws + p.off_rec);
+    a.N = N;
+    a.vocab = vocab;
+    a.chunks = p.chunks;
+    a.chunk_len = p.chunk_len;
+    a.topk = topk;
+    a.cap = cap;
+    a.groups = p.groups;
+    a.rec_words = p.rec_words;
+    const int epv = dtype == JF_BF16 ? 8 : 4;
+    a.aligned = (vocab % epv == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+    const int R = N > 1 ? N - 1 : 1;
+    const long grid = (long)B * R * p.chunks;
+    if (grid <= 0) return hipSuccess;
+    if (dtype == JF_BF16) {
+        switch (p.kt) {
+            case 1: launch_build_t<uint16_t, 1>(a, (int)grid, stream); break;
+            case 2: launch_build_t<uint16_t, 2>(a, (int)grid, stream); break;
+            case 4: launch_build_t<uint16_t, 4>(a, (int)grid, stream); break;
+            default: launch_build_t<uint16_t, 8>(a, (int)grid, stream); break;
+        }
+    } else {
+        switch (p.kt) {
+            case 1: launch_build_t<float, 1>(a, (int)grid, stream); break;
+            case 2: launch_build_t<float, 2>(a, (int)grid, stream); break;
+            case 4: launch_build_t<float, 4>(a, (int)grid, stream); break;
+            default: launch_build_t<float, 8>(a, (int)grid, stream); break;
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace jf
