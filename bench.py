@@ -71,13 +71,19 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --profile-steps into the traffic summary")
     ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--fork", action="store_true",
+                    help="run acceptance beside attention on a second stream (measured slower in graphs)")
     return ap.parse_args()
 
 
+ATTN_SOURCES = ("attn_bf16.hip", "jf_common.h")   # the attention kernel, its launch plan and shared helpers
+
+
 def source_digest():
-    """sha256 over the HIP sources and the public header (counters go stale when they change)."""
+    """sha256 over the attention kernel's sources and the public header (the
+    counters go stale when they change)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "tree_causal_attention_jf_amd", "csrc", "*"))) + \
+    files = [os.path.join(ROOT, "tree_causal_attention_jf_amd", "csrc", f) for f in ATTN_SOURCES] + \
         [os.path.join(ROOT, "include", "jf_tree.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -233,7 +239,11 @@ def time_graph(fn_list, reps, stream):
     return e0.elapsed_time(e1) / (reps * len(fn_list))
 
 
-def make_steps(jf, wl, sets, with_accept=True):
+def make_steps(jf, wl, sets, with_accept=True, side=None):
+    """Per-set callables for mask, attention, accept and the whole step. With a
+    side stream, a step forks after the mask: acceptance (which needs only the
+    ancestor bitset and the logits) runs on `side` while attention runs on the
+    current stream, and the current stream then waits for both."""
     def mask(s):
         return lambda: jf.build_ancestor_mask(s.t["parent"], anc=s.anc, depth=s.depth, bad_tree=s.bad)
 
@@ -249,11 +259,26 @@ def make_steps(jf, wl, sets, with_accept=True):
                                       bonus_token=s.bonus)
 
     def step(s):
-        fs = [mask(s), attn(s)] + ([accept(s)] if with_accept else [])
+        m, a, c = mask(s), attn(s), (accept(s) if with_accept else None)
 
         def run():
-            for f in fs:
-                f()
+            m()
+            if c is None:
+                a()
+            elif side is None:
+                a()
+                c()
+            else:
+                cur = torch.cuda.current_stream()
+                fork = torch.cuda.Event()
+                fork.record(cur)
+                side.wait_event(fork)
+                with torch.cuda.stream(side):
+                    c()
+                a()
+                join = torch.cuda.Event()
+                join.record(side)
+                cur.wait_event(join)
         return run
 
     return ([mask(s) for s in sets], [attn(s) for s in sets], [accept(s) for s in sets],
@@ -322,6 +347,39 @@ def time_paged_tree(jf, stream, seed=0):
                          "algorithmic_bytes": nbytes}}
 
 
+def time_build_tree(jf, stream, seed=0, B=8, N=256, vocab=151936, topk=4, cap=12):
+    """Best-first construction of the budget-256 trees from bf16 draft logits
+    [8, 256, 151936] (N(0, 2^2)), top-4 children, paths of at most 12 nodes.
+    Two logit sets (1.2 GB, beyond the 256 MB Infinity Cache) alternate.
+    Returns the JSON entry."""
+    from tree_causal_attention_jf_amd import workloads as W
+    case = W.make_draft_logits_case(seed, B, N, vocab, topk=topk, max_path_nodes=cap)
+    sets = [case.logits.cuda()]
+    sets.append(sets[0].roll(1, dims=0).contiguous())
+    outs = [(torch.empty((B, N), dtype=torch.int32, device="cuda"), torch.empty((B, N), dtype=torch.int32,
+             device="cuda"), torch.empty((B,), dtype=torch.int32, device="cuda")) for _ in sets]
+
+    def call(i):
+        return lambda: jf.build_tree(sets[i], topk, cap, parent=outs[i][0], token=outs[i][1], tree_len=outs[i][2],
+                                     return_score=False)
+    fns = [call(i) for i in range(len(sets))]
+    with torch.cuda.stream(stream):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    assert outs[0][2].cpu().tolist() == [N] * B
+    ms = time_graph(fns * 10, 20, stream)
+    # rows 0 .. N-2 are read (the last node to join offers no children)
+    nbytes = B * (N - 1) * vocab * sets[0].element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"batch {B}, budget {N}, bf16 draft logits [{B},{N},{vocab}] N(0,2^2), top-{topk} children, "
+                        f"paths of at most {cap} nodes",
+            "us": round(ms * 1e3, 3), "trees_per_s": round(B / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes},
+            "input_sets": len(sets)}
+
+
 def rotation_sets(wl, base, budget_bytes=2 * MALL_BYTES, cap=64):
     n = max(1, min(cap, math.ceil(budget_bytes / max(1, base.nbytes()))))
     return [base] + [DeviceSet(wl, src=base) for _ in range(n - 1)]
@@ -371,7 +429,10 @@ def main():
     sets = rotation_sets(wl, base)
     log(f"[bench] {len(sets)} input sets x {base.nbytes() / 1e6:.1f} MB")
     stream = torch.cuda.Stream()
-    masks, attns, accepts, steps = make_steps(jf, wl, sets)
+    side = torch.cuda.Stream() if args.fork else None
+    masks, attns, accepts, steps = make_steps(jf, wl, sets, side=side)
+    # the other submission form, measured beside the timed one
+    other_steps = make_steps(jf, wl, sets, side=None if args.fork else torch.cuda.Stream())[3]
 
     with torch.cuda.stream(stream):
         for i in range(max(1, args.warmup)):
@@ -403,11 +464,11 @@ def main():
     K = args.steps
     per = len(sets)
 
-    def capture(first, count):
+    def capture(first, count, fns=steps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(first, first + count):
-                steps[i % len(sets)]()
+                fns[i % len(sets)]()
         return g
 
     full = tail = None
@@ -445,6 +506,20 @@ def main():
         torch.cuda.synchronize()
         ms_step_single = (time.perf_counter() - t0) * 1e3 / K
         del singles
+    # the same steps in the other submission form (acceptance beside attention on a
+    # second stream, or after it on one stream)
+    ms_step_other = None
+    if not args.eager:
+        g = capture(0, per, other_steps)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, K // per)):
+                g.replay()
+        torch.cuda.synchronize()
+        ms_step_other = (time.perf_counter() - t0) * 1e3 / (max(1, K // per) * per)
+        del g
     chunks = full = tail = None
 
     # ---- per-kernel durations (graph of back-to-back launches, HIP events on the launch stream)
@@ -473,6 +548,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "ms_per_step_one_graph_per_step": round(ms_step_single, 6) if ms_step_single else None,
+        ("ms_per_step_accept_after_attention" if args.fork else "ms_per_step_accept_beside_attention"):
+            round(ms_step_other, 6) if ms_step_other else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -480,7 +557,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: Qwen3-8B attention layer, batch {wl.B}, {wl.N}-node chain, "
                                f"prefix {wl.max_prefix_len} in shuffled 16-token pages, {wl.Hq}q/{wl.Hkv}kv, "
-                               f"d={wl.D}; step = mask + attention + accept over {wl.vocab}-way bf16 logits",
+                               f"d={wl.D}; step = mask + attention + accept over {wl.vocab}-way bf16 logits"
+                               + (" (accept beside attention on a second stream)" if side is not None else ""),
                    "graph_replay": not args.eager, "steps_per_graph": 1 if args.eager else per,
                    "input_sets": len(sets)},
         "roofline": rl,
@@ -513,6 +591,28 @@ def main():
                          "hbm_GBps": round(nb2 / (t2 * 1e-3) / 1e9, 1), "flops": fl2, "algorithmic_bytes": nb2},
             "input_sets": len(sets2)}
         log(f"[bench] budget256: {t2 * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+
+    # ---- budget 16 where streaming the prefix sets the time: batch 8, prefix 16384
+    if not args.no_budget256:
+        log("[bench] building workload budget16_b8_16k")
+        wl5 = W.make_workload("c1_chain16", 0, B=8, prefix=("fixed", 16384), with_accept=False)
+        b5 = DeviceSet(wl5)
+        m5, a5, _, _ = make_steps(jf, wl5, [b5], with_accept=False)
+        with torch.cuda.stream(stream):
+            m5[0]()
+            a5[0]()
+        torch.cuda.synchronize()
+        nb5, fl5 = attention_work(wl5, b5.depth.cpu().numpy())
+        t5 = time_graph(a5 * 20, 20, stream)
+        gbs5 = nb5 / (t5 * 1e-3) / 1e9
+        result["budget16_streaming"] = {
+            "workload": "budget 16 at streaming size: batch 8, 16-node chains, prefix 16384 in shuffled 16-token "
+                        "pages, 32q/8kv, d=128 (537 MB of K/V per call, twice the Infinity Cache)",
+            "tree_tokens_per_s": round(wl5.B * wl5.N / (t5 * 1e-3), 1), "attention_us": round(t5 * 1e3, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs5, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs5 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nb5, "flops": fl5}}
+        log(f"[bench] budget16 streaming: {t5 * 1e3:.1f} us, {gbs5:.0f} GB/s")
+        del b5, m5, a5
 
     # ---- long context: batch 4, prefix 32768, 256-node trees; attention and acceptance timed apart
     if not args.no_long_context:
@@ -551,6 +651,13 @@ def main():
         result["ragged_budgets"] = time_paged_tree(jf, stream)
         log(f"[bench] ragged budgets: {result['ragged_budgets']['attention_us']} us, "
             f"{result['ragged_budgets']['roofline']['achieved']} TFLOP/s")
+
+    # ---- best-first tree construction from the draft logits (the step before verification)
+    if not args.no_budget256:
+        log("[bench] building draft logits for tree construction")
+        result["build_tree"] = time_build_tree(jf, stream)
+        log(f"[bench] build tree: {result['build_tree']['us']} us, "
+            f"{result['build_tree']['roofline']['achieved']} GB/s")
 
     # ---- commit of accepted paths into the paged cache (the step after acceptance)
     result["commit"] = [time_commit(jf, stream, *spec) for spec in (

@@ -353,6 +353,33 @@ def test_attention_bf16_large_sampled(jf, name):
         assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("B,lens,full", [
+    (4, [2048, 1500, 2100, 700], True),      # balanced batch: one 64-row block, two key groups
+    (1, [32768], False),                     # one sequence, long splits plus the tree's own split
+    (8, [16384] * 8, False),                 # the streaming budget-16 bench size, sampled rows
+], ids=["b4_ragged", "b1_32k", "b8_16k"])
+def test_attention_bf16_streaming_plan(jf, B, lens, full):
+    # 16-node chains x 4 query heads per KV head (64 rows) over prefixes long
+    # enough that streaming them sets the time: the plan switches to 64-row blocks
+    wl = W.make_workload("c1_chain16", 6, with_accept=False, B=B, prefix=("list", lens))
+    for unscaled in ((False, True) if full else (False,)):
+        if unscaled:
+            wl = W.make_workload("c1_chain16", 6, with_accept=False, B=B, prefix=("list", lens), unscaled=True)
+        out, lse = run_attention(jf, wl, to_dev(wl))
+        rows = None if full else _sampled_rows(wl, 48, 2)
+        ref, lref = _oracle_full(wl, rows=rows)
+        if full:
+            check_bf16(out, ref, lse, lref, f"streaming B {B}{' unscaled' if unscaled else ''}",
+                       abs_tol=derived_bf16_bar(wl))
+        else:
+            o = out.float().cpu().numpy()
+            idx = tuple(np.array(rows).T)
+            check_bf16(torch.from_numpy(o[idx]), ref[idx], lse.cpu()[idx], lref[idx],
+                       f"streaming B {B}{' unscaled' if unscaled else ''} ({len(rows)} rows)",
+                       abs_tol=derived_bf16_bar(wl))
+            assert torch.isfinite(out.float()).all()
+
+
 def test_attention_bf16_batch_with_long_prefix(jf):
     # a batch whose longest prefix needs more than one split's page list (1024 pages):
     # the balanced plan must give that sequence at least ceil(pages / 1024) pieces
@@ -466,3 +493,67 @@ def test_graph_replay_matches_eager(jf):
         step(eager)                                       # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(eager["out"].view(torch.int16), ref_out.view(torch.int16)), rep
+
+
+def test_forked_step_graph_matches_serial(jf):
+    """Acceptance forked onto a second stream after the mask, beside attention,
+    captured in one graph with several steps: every replay equals the serial
+    eager step bit for bit."""
+    wl = W.make_workload("c1_chain16", 4, with_accept=True)
+    d = to_dev(wl)
+    s, side = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def make_bufs():
+        return dict(anc=torch.empty((wl.B, wl.N, 4), dtype=torch.uint64, device=DEV),
+                    out=torch.empty_like(d["q"]),
+                    acc=[torch.empty((wl.B,), dtype=torch.int32, device=DEV),
+                         torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV),
+                         torch.empty((wl.B,), dtype=torch.int32, device=DEV),
+                         torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV)])
+
+    def accept(o):
+        a = o["acc"]
+        jf.tree_accept(d["parent"], o["anc"], d["draft"], logits=d["logits"], accept_len=a[0],
+                       accepted_nodes=a[1], bonus_token=a[2], next_tokens=a[3])
+
+    def attn(o):
+        jf.tree_attention(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["prefix_len"], d["k_tree"],
+                          d["v_tree"], o["anc"], sm_scale=wl.sm_scale, max_prefix_len=wl.max_prefix_len,
+                          out=o["out"])
+
+    def forked(o):
+        cur = torch.cuda.current_stream()
+        jf.build_ancestor_mask(d["parent"], anc=o["anc"], with_depth=False)
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            accept(o)
+        attn(o)
+        join = torch.cuda.Event()
+        join.record(side)
+        cur.wait_event(join)
+
+    ref = make_bufs()
+    jf.build_ancestor_mask(d["parent"], anc=ref["anc"], with_depth=False)
+    attn(ref)
+    accept(ref)
+    torch.cuda.synchronize()
+    bufs = [make_bufs() for _ in range(3)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for o in bufs:
+            forked(o)
+    for rep in range(4):
+        for o in bufs:
+            o["out"].zero_()
+            for t in o["acc"]:
+                t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for o in bufs:
+            assert torch.equal(o["out"].view(torch.int16), ref["out"].view(torch.int16)), rep
+            for a, b in zip(o["acc"], ref["acc"]):
+                assert torch.equal(a, b), rep
+        accept(ref)                                        # eager work between replays
+        torch.cuda.synchronize()

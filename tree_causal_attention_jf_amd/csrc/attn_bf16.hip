@@ -1039,6 +1039,19 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     else if (rows <= 128) { p.rw = 4; p.kw = 2; }
     else { p.rw = 8; p.kw = 1; }   // (128-row blocks hold one prefetch round: slower)
     p.rpw = 1;
+    {
+        // Few rows but many tiles per workgroup: streaming the prefix sets the time.
+        // Then one 64-row block (both row groups share every K/V tile read) with two
+        // key groups (a second round of tiles in flight while one is consumed) beats
+        // 32-row blocks with four key groups, which read each tile twice and drain
+        // the ring every round. Measured at 16 tree nodes x 4 heads per KV head:
+        // batch 8 x 16384 prefix 157 -> 104 us; at batch 1 x 2048 (2 tiles per
+        // workgroup) the four key groups stay ahead (15.2 vs 19.8 us).
+        const long pages = (max_prefix + kPage - 1) / kPage;
+        const long tiles_per_wg = (long)s.B * s.Hkv * ((rows + 31) / 32) * ((pages + 3) / 4) / 256;
+        if (rows <= 64 && tiles_per_wg >= env_int(s.B >= 2 ? "JF_STREAM_TILES" : "JF_STREAM_TILES1",
+                                                  s.B >= 2 ? 8 : 32)) { p.rw = 2; p.kw = 2; }
+    }
     // tuning override: JF_RW = 1, 2, 4 or 8 row groups (key groups follow)
     switch (env_int("JF_RW", 0)) {
         case 1: p.rw = 1; p.kw = 4; break;
@@ -1058,7 +1071,9 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     p.cus = target > 0 ? target : 256;
     // at least one full round of tiles per split
     const int min_pages = 4 * p.kw;
-    int splits = p.items > 0 ? (target + p.items - 1) / p.items : 1;
+    // one workgroup per CU: never more workgroups than the target (a second wave of
+    // a few workgroups would double the time)
+    int splits = p.items > 0 ? target / p.items : 1;
     int max_splits = max_pages > 0 ? (max_pages + min_pages - 1) / min_pages : 1;
     if (max_splits > kMaxSplits) max_splits = kMaxSplits;
     splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
@@ -1098,6 +1113,18 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
     // of adding a round (and a full memory latency) to the last prefix split
     if (!p.balanced && splits > 1 && p.pps / 4 <= 8 * p.kw && env_int("JF_TREE_SPLIT", 1) &&
         (size_t)p.items * (splits + 1) * p.rb * s.D * 4 < (size_t)0xffffff00u) {
+        // room for the tree's split within the target: fewer, longer prefix splits
+        while (forced <= 0 && splits > 1 && (long)p.items * (splits + 1) > target) {
+            int fewer = splits - 1;
+            int longer = (max_pages + fewer - 1) / fewer;
+            longer = (longer + 3) / 4 * 4;
+            if (longer > kMaxPagesPerSplit) break;          // splits already as long as they may be
+            fewer = (max_pages + longer - 1) / longer;
+            if (fewer >= splits) break;
+            splits = fewer;
+            pps = longer;
+        }
+        p.pps = pps;
         p.tree_split = 1;
         splits += 1;
         p.splits = splits;
