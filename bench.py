@@ -71,8 +71,8 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --profile-steps into the traffic summary")
     ap.add_argument("--no-long-context", action="store_true")
-    ap.add_argument("--fork", action="store_true",
-                    help="run acceptance beside attention on a second stream (measured slower in graphs)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time steps as mask + jf_tree_attention + jf_tree_accept instead of mask + jf_tree_verify")
     return ap.parse_args()
 
 
@@ -239,11 +239,11 @@ def time_graph(fn_list, reps, stream):
     return e0.elapsed_time(e1) / (reps * len(fn_list))
 
 
-def make_steps(jf, wl, sets, with_accept=True, side=None):
-    """Per-set callables for mask, attention, accept and the whole step. With a
-    side stream, a step forks after the mask: acceptance (which needs only the
-    ancestor bitset and the logits) runs on `side` while attention runs on the
-    current stream, and the current stream then waits for both."""
+def make_steps(jf, wl, sets, with_accept=True, fused=True):
+    """Per-set callables for mask, attention, accept and the whole step. A step is
+    the mask, then attention and acceptance: with `fused`, one jf_tree_verify
+    call (attention and acceptance in one launch where the plan allows it),
+    otherwise jf_tree_attention followed by jf_tree_accept."""
     def mask(s):
         return lambda: jf.build_ancestor_mask(s.t["parent"], anc=s.anc, depth=s.depth, bad_tree=s.bad)
 
@@ -258,27 +258,25 @@ def make_steps(jf, wl, sets, with_accept=True, side=None):
                                       next_tokens=s.nxt, accept_len=s.alen, accepted_nodes=s.nodes,
                                       bonus_token=s.bonus)
 
+    def verify(s):
+        return lambda: jf.tree_verify(s.t["q"], s.t["k_pages"], s.t["v_pages"], s.t["block_table"],
+                                      s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], s.anc, s.t["parent"],
+                                      s.t["draft"], s.t["logits"], sm_scale=wl.sm_scale,
+                                      max_prefix_len=wl.max_prefix_len, out=s.out, next_tokens=s.nxt,
+                                      accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus)
+
     def step(s):
-        m, a, c = mask(s), attn(s), (accept(s) if with_accept else None)
+        m, a = mask(s), attn(s)
+        if not with_accept:
+            fs = [m, a]
+        elif fused and s.t["logits"] is not None:
+            fs = [m, verify(s)]
+        else:
+            fs = [m, a, accept(s)]
 
         def run():
-            m()
-            if c is None:
-                a()
-            elif side is None:
-                a()
-                c()
-            else:
-                cur = torch.cuda.current_stream()
-                fork = torch.cuda.Event()
-                fork.record(cur)
-                side.wait_event(fork)
-                with torch.cuda.stream(side):
-                    c()
-                a()
-                join = torch.cuda.Event()
-                join.record(side)
-                cur.wait_event(join)
+            for f in fs:
+                f()
         return run
 
     return ([mask(s) for s in sets], [attn(s) for s in sets], [accept(s) for s in sets],
@@ -429,10 +427,9 @@ def main():
     sets = rotation_sets(wl, base)
     log(f"[bench] {len(sets)} input sets x {base.nbytes() / 1e6:.1f} MB")
     stream = torch.cuda.Stream()
-    side = torch.cuda.Stream() if args.fork else None
-    masks, attns, accepts, steps = make_steps(jf, wl, sets, side=side)
-    # the other submission form, measured beside the timed one
-    other_steps = make_steps(jf, wl, sets, side=None if args.fork else torch.cuda.Stream())[3]
+    masks, attns, accepts, steps = make_steps(jf, wl, sets, fused=not args.separate)
+    # the other form of the step, measured beside the timed one
+    other_steps = make_steps(jf, wl, sets, fused=args.separate)[3]
 
     with torch.cuda.stream(stream):
         for i in range(max(1, args.warmup)):
@@ -506,8 +503,8 @@ def main():
         torch.cuda.synchronize()
         ms_step_single = (time.perf_counter() - t0) * 1e3 / K
         del singles
-    # the same steps in the other submission form (acceptance beside attention on a
-    # second stream, or after it on one stream)
+    # the same steps in the other form (separate attention and acceptance launches,
+    # or the one verification call)
     ms_step_other = None
     if not args.eager:
         g = capture(0, per, other_steps)
@@ -527,8 +524,15 @@ def main():
     t_mask = time_graph(masks, reps, stream)
     t_attn = time_graph(attns, reps, stream)
     t_acc = time_graph(accepts, reps, stream)
+    verifies = [(lambda s=s: jf.tree_verify(s.t["q"], s.t["k_pages"], s.t["v_pages"], s.t["block_table"],
+                                            s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], s.anc, s.t["parent"],
+                                            s.t["draft"], s.t["logits"], sm_scale=wl.sm_scale,
+                                            max_prefix_len=wl.max_prefix_len, out=s.out, next_tokens=s.nxt,
+                                            accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus))
+                for s in sets] if wl.logits is not None else None
+    t_ver = time_graph(verifies, reps, stream) if verifies else None
     log(f"[bench] per launch: mask {t_mask * 1e3:.2f} us, attention {t_attn * 1e3:.2f} us, "
-        f"accept {t_acc * 1e3:.2f} us")
+        f"accept {t_acc * 1e3:.2f} us, verify (attention + accept) {t_ver * 1e3 if t_ver else 0:.2f} us")
     achieved = nbytes / (t_attn * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.config)
     rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -548,7 +552,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "ms_per_step_one_graph_per_step": round(ms_step_single, 6) if ms_step_single else None,
-        ("ms_per_step_accept_after_attention" if args.fork else "ms_per_step_accept_beside_attention"):
+        ("ms_per_step_verify_call" if args.separate else "ms_per_step_separate_launches"):
             round(ms_step_other, 6) if ms_step_other else None,
         "higher_is_better": True,
         "scaling": "weak",
@@ -558,12 +562,14 @@ def main():
         "config": {"workload": f"{args.config}: Qwen3-8B attention layer, batch {wl.B}, {wl.N}-node chain, "
                                f"prefix {wl.max_prefix_len} in shuffled 16-token pages, {wl.Hq}q/{wl.Hkv}kv, "
                                f"d={wl.D}; step = mask + attention + accept over {wl.vocab}-way bf16 logits"
-                               + (" (accept beside attention on a second stream)" if side is not None else ""),
+                               + (" (separate launches)" if args.separate else
+                                  " (jf_tree_verify: attention and acceptance in one launch)"),
                    "graph_replay": not args.eager, "steps_per_graph": 1 if args.eager else per,
                    "input_sets": len(sets)},
         "roofline": rl,
         "kernels_us": {"build_ancestor_mask": round(t_mask * 1e3, 3), "tree_attention": round(t_attn * 1e3, 3),
                        "tree_accept": round(t_acc * 1e3, 3),
+                       "tree_verify": round(t_ver * 1e3, 3) if t_ver else None,
                        "accept_GBps": round(logit_bytes / (t_acc * 1e-3) / 1e9, 1) if logit_bytes else None},
     }
 

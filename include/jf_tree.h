@@ -237,6 +237,38 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * jf_tree_verify -- one tree-verification step: jf_tree_attention and
+ * jf_tree_accept (logits mode) together (technical summaries, section 3:
+ * tree verification over a paged KV cache; lay summary: keep the drafted
+ * tokens up to the first disagreement).
+ *
+ * Arguments as in those two calls: the attention arguments with the
+ * attention workspace (size from jf_tree_attention_workspace_bytes), then
+ * vocab, target_logits (required) with logits_dtype, draft_tokens, parent,
+ * the four acceptance outputs and the acceptance workspace (size from
+ * jf_tree_accept_workspace_bytes). Both read the same anc. The results are
+ * exactly those of jf_tree_attention followed by jf_tree_accept.
+ *
+ * With bf16 attention, bf16 logits and a plan whose attention workgroups
+ * have four waves (few query rows per KV head, as at budget 16), both run in
+ * one launch and side by side on the chip; otherwise the two launches follow
+ * each other on the stream. The two workspaces must not overlap: each keeps
+ * the rules of its own call (counter region zeroed once, left zero).
+ *
+ * Host errors: those of jf_tree_attention and of jf_tree_accept, plus
+ * JF_ERR_NULL (target_logits NULL) and JF_ERR_WORKSPACE (overlapping
+ * workspaces).
+ */
+jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
+                         const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                         const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                         void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
+                         const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
+                         const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                         int32_t* accepted_nodes, int32_t* bonus_token, void* accept_workspace,
+                         size_t accept_workspace_bytes, hipStream_t stream);
+
+/*
  * jf_commit_accepted -- append each sequence's accepted path to its paged KV
  * cache, the step after acceptance (lay summary: the target keeps the drafted
  * tokens up to its first disagreement; technical summary, section 3: the

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
                "jf_commit_accepted", "jf_tree_attention_paged_tree", "jf_build_tree",
-               "jf_build_tree_workspace_bytes"):
+               "jf_build_tree_workspace_bytes", "jf_tree_verify"):
         assert fn in names
 
 
@@ -259,3 +259,37 @@ def test_build_tree_host_checks(binding):
     assert call(ws=ctypes.c_void_p(0)) == JF_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(4104)) == JF_ERR_ALIGN
     assert call(B=0) == JF_OK                                                  # empty batch: no launch
+
+
+def test_verify_host_checks(binding):
+    """jf_tree_verify applies the checks of both calls it stands for, needs the
+    logits, and refuses overlapping workspaces; all before any launch."""
+    L = binding._lib
+    shape = _shape(binding)
+    a_need = binding.tree_attention_workspace_bytes(shape, 2048)
+    c_need = binding.tree_accept_workspace_bytes(1, 16, 1000)
+    p = ctypes.c_void_p(16)
+
+    def ver(shape=shape, max_prefix=2048, logits=p, dt=1, V=1000, aws=0x100000, awsb=a_need, cws=0x800000,
+            cwsb=c_need, nul=()):
+        a = {n: p for n in ("q", "kp", "vp", "bt", "pl", "kt", "vt", "anc", "out", "draft", "parent", "next",
+                            "alen", "nodes", "bonus")}
+        for n in nul:
+            a[n] = None
+        return L.jf_tree_verify(ctypes.byref(shape), max_prefix, a["q"], a["kp"], a["vp"], a["bt"], a["pl"],
+                                a["kt"], a["vt"], a["anc"], a["out"], None, ctypes.c_void_p(aws), awsb, V, logits,
+                                dt, a["draft"], a["parent"], a["next"], a["alen"], a["nodes"], a["bonus"],
+                                ctypes.c_void_p(cws), cwsb, None)
+
+    assert ver(shape=_shape(binding, N=0)) == JF_ERR_SHAPE          # attention's checks
+    assert ver(shape=_shape(binding, D=96)) == JF_ERR_UNSUPPORTED
+    assert ver(logits=None) == JF_ERR_NULL                          # logits are required
+    assert ver(dt=5) == JF_ERR_DTYPE                                # acceptance's checks
+    assert ver(V=0) == JF_ERR_SHAPE
+    for n in ("q", "anc", "out", "draft", "parent", "next", "alen", "nodes", "bonus"):
+        assert ver(nul=(n,)) == JF_ERR_NULL, n
+    assert ver(awsb=a_need - 1) == JF_ERR_WORKSPACE
+    assert ver(cwsb=c_need - 1) == JF_ERR_WORKSPACE
+    assert ver(cws=0x100000 + a_need - 256) == JF_ERR_WORKSPACE     # overlapping workspaces
+    assert ver(aws=0x800000 + 256) == JF_ERR_WORKSPACE
+    assert ver(shape=_shape(binding, B=0)) == JF_OK                 # empty batch: no launch

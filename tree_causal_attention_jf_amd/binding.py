@@ -38,6 +38,7 @@ EXPORTED = (
     "jf_tree_attention_paged_tree",
     "jf_build_tree_workspace_bytes",
     "jf_build_tree",
+    "jf_tree_verify",
 )
 
 
@@ -84,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_accept_workspace_bytes.argtypes = [i32, i32, i32]
     lib.jf_tree_accept.restype = i32
     lib.jf_tree_accept.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jf_tree_verify.restype = i32
+    lib.jf_tree_verify.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   vp, sz, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.jf_tree_attention_paged_tree.restype = i32
     lib.jf_tree_attention_paged_tree.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp, sz, vp]
@@ -299,6 +303,56 @@ def tree_accept(parent, anc, draft, logits: Optional[torch.Tensor] = None,
                              _ptr(bonus_token), _ptr(ws), ws_bytes, _stream(dev))
     _check("jf_tree_accept", st)
     return accept_len, accepted_nodes, bonus_token, next_tokens
+
+
+def tree_verify(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc, parent, draft, logits,
+                sm_scale: Optional[float] = None, max_prefix_len: Optional[int] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                next_tokens=None, accept_len=None, accepted_nodes=None, bonus_token=None,
+                attn_workspace: Optional[torch.Tensor] = None, accept_workspace: Optional[torch.Tensor] = None):
+    """One verification step: tree attention and acceptance over the target logits
+    (see include/jf_tree.h). Returns (out, lse or None, accept_len, accepted_nodes,
+    bonus_token, next_tokens)."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (k_tree, "k_tree"), (v_tree, "v_tree")):
+        _need(t, n, q.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(prefix_len, "prefix_len", torch.int32)
+    _need(anc, "anc", torch.uint64)
+    _need(parent, "parent", torch.int32)
+    _need(draft, "draft", torch.int32)
+    _need(logits, "logits")
+    ldt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}[logits.dtype]
+    shape = attn_shape(q, k_pages, block_table, sm_scale)
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_len.max().item()) if prefix_len.numel() else 0
+    dev = q.device
+    B, N = parent.shape
+    vocab = logits.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if next_tokens is None:
+        next_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if bonus_token is None:
+        bonus_token = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = tree_attention_workspace_bytes(shape, max_prefix_len)
+    aws = attn_workspace if attn_workspace is not None else _default_ws.get(dev, "attn", need)
+    aws_bytes = 0 if aws is None else aws.numel() * aws.element_size()
+    cws = accept_workspace if accept_workspace is not None else \
+        _default_ws.get(dev, "accept", tree_accept_workspace_bytes(B, N, vocab))
+    cws_bytes = cws.numel() * cws.element_size()
+    st = _lib.jf_tree_verify(ctypes.byref(shape), int(max_prefix_len), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                             _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(out),
+                             _ptr(lse), _ptr(aws), aws_bytes, vocab, _ptr(logits), ldt, _ptr(draft), _ptr(parent),
+                             _ptr(next_tokens), _ptr(accept_len), _ptr(accepted_nodes), _ptr(bonus_token),
+                             _ptr(cws), cws_bytes, _stream(dev))
+    _check("jf_tree_verify", st)
+    return out, lse, accept_len, accepted_nodes, bonus_token, next_tokens
 
 
 def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len, k_pages, v_pages,

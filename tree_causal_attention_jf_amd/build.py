@@ -37,7 +37,7 @@ def _hipcc() -> str:
 # Kernels whose loops count their own vector-memory operations (s_waitcnt vmcnt
 # with hand-computed limits): a register spill would add scratch loads to that
 # count and let a wait return early, so such a kernel must use no scratch.
-NO_SCRATCH_KERNELS = ("tree_attn_bf16_kernel",)
+NO_SCRATCH_KERNELS = ("tree_attn_bf16_kernel", "tree_verify_bf16_kernel")
 
 
 def _run(cmd, verbose):

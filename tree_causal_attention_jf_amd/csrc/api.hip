@@ -23,6 +23,14 @@ hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype,
                          int32_t* accept_len, int32_t* accepted_nodes, int32_t* bonus, void* workspace,
                          hipStream_t stream);
 size_t accept_workspace_bytes(int B, int N, int vocab);
+hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                              const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                              void* attn_workspace, int vocab, const void* logits, const int32_t* draft,
+                              const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                              int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
+                              hipStream_t stream);
+bool verify_fusable(const jf_attn_shape& s, int max_prefix, int logits_dtype);
 hipError_t launch_commit(const jf_attn_shape& s, const void* k_tree, const void* v_tree, const int32_t* accept_len,
                          const int32_t* accepted_nodes, const int32_t* block_table, const int32_t* prefix_len,
                          void* k_pages, void* v_pages, int32_t* new_prefix_len, hipStream_t stream);
@@ -91,10 +99,12 @@ size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_pre
     return jf::attention_bf16_workspace_bytes(*s, max_prefix_len);
 }
 
-jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
-                            const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
-                            const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Host checks of jf_tree_attention (nothing is launched).
+static jf_status check_attention_call(const jf_attn_shape* s, int32_t max_prefix_len, const void* q,
+                                      const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                      const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                                      const uint64_t* anc, const void* out, const void* workspace,
+                                      size_t workspace_bytes) {
     const jf_status st = check_attn_shape(s, max_prefix_len);
     if (st != JF_OK) return st;
     if (!q || !prefix_len || !k_tree || !v_tree || !anc || !out) return JF_ERR_NULL;
@@ -107,6 +117,16 @@ jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len, cons
         if (!workspace || workspace_bytes < need) return JF_ERR_WORKSPACE;
         if (!aligned16(workspace)) return JF_ERR_ALIGN;
     }
+    return JF_OK;
+}
+
+jf_status jf_tree_attention(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                            const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const jf_status st = check_attention_call(s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,
+                                              k_tree, v_tree, anc, out, workspace, workspace_bytes);
+    if (st != JF_OK) return st;
     if (s->B == 0) return JF_OK;
     hipError_t e;
     if (s->dtype == JF_BF16)
@@ -145,10 +165,12 @@ size_t jf_tree_accept_workspace_bytes(int32_t B, int32_t N, int32_t vocab) {
     return jf::accept_workspace_bytes(B, N, vocab);
 }
 
-jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target_logits, int32_t logits_dtype,
-                         const int32_t* target_ids, const int32_t* draft_tokens, const int32_t* parent,
-                         const uint64_t* anc, int32_t* next_tokens, int32_t* accept_len, int32_t* accepted_nodes,
-                         int32_t* bonus_token, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Host checks of jf_tree_accept (nothing is launched).
+static jf_status check_accept_call(int32_t B, int32_t N, int32_t vocab, const void* target_logits,
+                                   int32_t logits_dtype, const int32_t* target_ids, const int32_t* draft_tokens,
+                                   const int32_t* parent, const uint64_t* anc, const int32_t* next_tokens,
+                                   const int32_t* accept_len, const int32_t* accepted_nodes,
+                                   const int32_t* bonus_token, const void* workspace, size_t workspace_bytes) {
     if (B < 0 || N < 1 || N > JF_MAX_NODES || vocab < 1) return JF_ERR_SHAPE;
     if ((target_logits == nullptr) == (target_ids == nullptr)) return JF_ERR_SHAPE;
     if (!draft_tokens || !parent || !anc || !next_tokens || !accept_len || !accepted_nodes || !bonus_token)
@@ -161,10 +183,64 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target
         if ((long)B * N * ((vocab + 4095) / 4096) > 0x7fffffffL) return JF_ERR_SHAPE;
         if (B > JF_WORKSPACE_COUNTER_BYTES / 4) return JF_ERR_SHAPE;   // one counter per sequence
     }
+    return JF_OK;
+}
+
+jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target_logits, int32_t logits_dtype,
+                         const int32_t* target_ids, const int32_t* draft_tokens, const int32_t* parent,
+                         const uint64_t* anc, int32_t* next_tokens, int32_t* accept_len, int32_t* accepted_nodes,
+                         int32_t* bonus_token, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const jf_status st = check_accept_call(B, N, vocab, target_logits, logits_dtype, target_ids, draft_tokens,
+                                           parent, anc, next_tokens, accept_len, accepted_nodes, bonus_token,
+                                           workspace, workspace_bytes);
+    if (st != JF_OK) return st;
     if (B == 0) return JF_OK;
     const hipError_t e = jf::launch_accept(B, N, vocab, target_logits, logits_dtype, target_ids, draft_tokens,
                                            parent, anc, next_tokens, accept_len, accepted_nodes, bonus_token,
                                            workspace, stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
+                         const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                         const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                         void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
+                         const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
+                         const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                         int32_t* accepted_nodes, int32_t* bonus_token, void* accept_workspace,
+                         size_t accept_workspace_bytes, hipStream_t stream) {
+    jf_status st = check_attention_call(s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                        v_tree, anc, out, attn_workspace, attn_workspace_bytes);
+    if (st != JF_OK) return st;
+    if (!target_logits) return JF_ERR_NULL;
+    st = check_accept_call(s->B, s->N, vocab, target_logits, logits_dtype, nullptr, draft_tokens, parent, anc,
+                           next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace,
+                           accept_workspace_bytes);
+    if (st != JF_OK) return st;
+    const size_t attn_need = jf_tree_attention_workspace_bytes(s, max_prefix_len);
+    if (attn_need > 0) {
+        const char* a0 = static_cast<const char*>(attn_workspace);
+        const char* c0 = static_cast<const char*>(accept_workspace);
+        const size_t acc_need = jf::accept_workspace_bytes(s->B, s->N, vocab);
+        if (a0 < c0 + acc_need && c0 < a0 + attn_need) return JF_ERR_WORKSPACE;
+    }
+    if (s->B == 0) return JF_OK;
+    hipError_t e;
+    if (jf::verify_fusable(*s, max_prefix_len, logits_dtype)) {
+        e = jf::launch_verify_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree,
+                                   anc, out, lse, attn_workspace, vocab, target_logits, draft_tokens, parent,
+                                   next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace, stream);
+    } else {
+        e = s->dtype == JF_BF16
+                ? jf::launch_attention_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,
+                                            k_tree, v_tree, anc, out, lse, attn_workspace, stream)
+                : jf::launch_attention_f32(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,
+                                           k_tree, v_tree, anc, out, lse, stream);
+        if (e == hipSuccess)
+            e = jf::launch_accept(s->B, s->N, vocab, target_logits, logits_dtype, nullptr, draft_tokens, parent,
+                                  anc, next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace,
+                                  stream);
+    }
     return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
 }
 

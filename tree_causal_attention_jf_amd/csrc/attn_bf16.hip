@@ -52,6 +52,7 @@
 // per 32-key block, so the 256-bit ancestor bitset of that row's node sits in
 // the lane's registers and masking is a per-register bit test.
 #include "jf_common.h"
+#include "accept_device.h"
 
 namespace jf {
 
@@ -128,6 +129,15 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* gptr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
                  : "memory", "m0");
+}
+
+// A pointer the compiler may not prove wave-uniform (it is, by construction) in scalar registers.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
 // The same from a wave-uniform base (scalar registers) plus a per-lane 32-bit byte offset.
@@ -215,6 +225,7 @@ __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* 
             // prefix tiles start on page boundaries; s_pages[k] = page of the split's k-th 16 tokens
             const int page = __builtin_amdgcn_readfirstlane(s_pages[it * (kKeyTile / kPage) + pq]);
             const uint16_t* base = (isv ? vp : kp) + ((long)page * Hkv + kvh) * (kPage * D);
+            base = uniform_ptr(base);                    // wave-uniform by construction
             #pragma unroll
             for (int kb = 0; kb < TPP; ++kb)
                 dma16_s(__builtin_amdgcn_readfirstlane(lds0 + kb * 1024), base, isv ? pl.v[kb] : pl.k[kb]);
@@ -445,8 +456,10 @@ __device__ __forceinline__ uint32_t part_off(int r, int c) {
         return (uint32_t)(r * D + c * 4);
 }
 
+// Workgroup `bid` of an attention grid of `nblk` workgroups (the attention
+// launch, or the attention part of the fused verification launch).
 template <int D, int RW, int KW, int RPW>
-__global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const unsigned bid, const unsigned nblk) {
     using Gm = Geo<D>;
     constexpr bool kFragPart = KW == 1;              // split partial layout (part_off)
     constexpr int NW = RW * KW;
@@ -511,8 +524,8 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
                 const int kj = __shfl(key, j), nj = __shfl(n, j);
                 off += (kj > key || (kj == key && j < lane)) ? nj : 0;
             }
-            const int slot = blockIdx.x / kNumXcd;
-            const int u = (slot / a.nrb) * kNumXcd + blockIdx.x % kNumXcd;
+            const int slot = bid / kNumXcd;
+            const int u = (slot / a.nrb) * kNumXcd + bid % kNumXcd;
             const int lo = off * a.Hkv;
             const bool mine = lane < a.B && u >= lo && u < lo + n * a.Hkv;
             if (mine) {
@@ -529,10 +542,10 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
         s = __builtin_amdgcn_readfirstlane(s_plan[1]);
         kvh = __builtin_amdgcn_readfirstlane(s_plan[2]);
         pps = __builtin_amdgcn_readfirstlane(s_plan[3]);
-        rb = (blockIdx.x / kNumXcd) % a.nrb;
+        rb = (bid / kNumXcd) % a.nrb;
     } else {
         // ids remapped so that one KV head's row blocks and splits share an XCD
-        const int lid = xcd_remap(blockIdx.x, gridDim.x);
+        const int lid = xcd_remap(bid, nblk);
         rb = lid % a.nrb;
         int t1 = lid / a.nrb;
         s = t1 % a.splits;
@@ -1008,6 +1021,11 @@ __global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a
     }
 }
 
+template <int D, int RW, int KW, int RPW>
+__global__ __launch_bounds__(RW * KW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
+    tree_attn_bf16_body<D, RW, KW, RPW>(a, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------- host side
 
 struct AttnPlanBf16 {
@@ -1157,13 +1175,12 @@ static hipError_t launch_bf16_d(const AttnPlanBf16& p, const AttnArgs& a, hipStr
     return launch_bf16_t<D, 8, 1, 1>(a, p.grid, stream);
 }
 
-hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
-                                 const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
-                                 const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
-                                 float* lse, void* workspace, hipStream_t stream, const int32_t* tree_len,
-                                 int paged_tree) {
-    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
-    if (p.grid == 0) return hipSuccess;
+// Kernel arguments of one attention call under plan p.
+static AttnArgs make_attn_args(const AttnPlanBf16& p, const jf_attn_shape& s, int max_prefix, const void* q,
+                               const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                               const uint64_t* anc, void* out, float* lse, void* workspace,
+                               const int32_t* tree_len, int paged_tree) {
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.kp = static_cast<const uint16_t*>(k_pages);
@@ -1204,13 +1221,88 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
     a.tree_split = p.tree_split;
     a.tree_len = tree_len;
     a.paged_tree = paged_tree;
+    a.scale_log2 = s.sm_scale * 1.44269504088896340736f;
+    return a;
+}
+
+// Counters past the fixed region (more than kMaxCounters items with splits) are
+// zero-filled by a small kernel before the attention launch.
+static void fill_counters(const AttnPlanBf16& p, void* workspace, hipStream_t stream) {
     if (p.splits > 1 && p.fill_bytes > 0) {
         const int n = (int)(p.fill_bytes / 4);
         hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream,
-                           reinterpret_cast<int*>(ws + kCounterBytes), n);
+                           reinterpret_cast<int*>(static_cast<char*>(workspace) + kCounterBytes), n);
     }
-    a.scale_log2 = s.sm_scale * 1.44269504088896340736f;
+}
+
+hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
+                                 const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                                 const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
+                                 float* lse, void* workspace, hipStream_t stream, const int32_t* tree_len,
+                                 int paged_tree) {
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    if (p.grid == 0) return hipSuccess;
+    const AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                      v_tree, anc, out, lse, workspace, tree_len, paged_tree);
+    fill_counters(p, workspace, stream);
     return s.D == 128 ? launch_bf16_d<128>(p, a, stream) : launch_bf16_d<64>(p, a, stream);
+}
+
+// ---------------------------------------------------------------- fused verification
+
+// Attention and acceptance in one grid: workgroups [0, attn_grid) run the
+// attention body, the rest (one per logits row and vocabulary chunk) the
+// argmax + walk. The two parts share nothing but the launch: neither waits
+// for the other, so on a chip with more CUs than the attention grid fills they
+// run side by side instead of one after the other. Needs 256-thread attention
+// workgroups (four waves), the acceptance workgroup size.
+template <int D, int RW, int KW, int RPW>
+__global__ __launch_bounds__(RW * KW * 64) void tree_verify_bf16_kernel(AttnArgs a, AcceptArgs c,
+                                                                         unsigned attn_grid) {
+    static_assert(RW * KW * 64 == kAcceptThreads, "the two parts share the workgroup size");
+    if (blockIdx.x < attn_grid) tree_attn_bf16_body<D, RW, KW, RPW>(a, blockIdx.x, attn_grid);
+    else accept_logits_body<uint16_t>(c, (int)(blockIdx.x - attn_grid));
+}
+
+template <int D, int RW, int KW, int RPW>
+static hipError_t launch_verify_t(const AttnArgs& a, const AcceptArgs& c, long attn_grid, long accept_grid,
+                                  hipStream_t stream) {
+    hipLaunchKernelGGL((tree_verify_bf16_kernel<D, RW, KW, RPW>), dim3((unsigned)(attn_grid + accept_grid)),
+                       dim3(RW * KW * 64), 0, stream, a, c, (unsigned)attn_grid);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_verify_d(const AttnPlanBf16& p, const AttnArgs& a, const AcceptArgs& c, long accept_grid,
+                                  hipStream_t stream) {
+    if (p.rpw == 2) return launch_verify_t<D, 4, 1, 2>(a, c, p.grid, accept_grid, stream);
+    if (p.rw == 1) return launch_verify_t<D, 1, 4, 1>(a, c, p.grid, accept_grid, stream);
+    return launch_verify_t<D, 2, 2, 1>(a, c, p.grid, accept_grid, stream);
+}
+
+bool verify_fusable(const jf_attn_shape& s, int max_prefix, int logits_dtype) {
+    if (s.dtype != JF_BF16 || logits_dtype != JF_BF16 || s.B == 0) return false;
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    return p.grid > 0 && p.rw * p.kw == 4 && (p.rpw == 1 || p.rpw == 2);
+}
+
+hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
+                              const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
+                              void* attn_workspace, int vocab, const void* logits, const int32_t* draft,
+                              const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                              int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
+                              hipStream_t stream) {
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    const AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                      v_tree, anc, out, lse, attn_workspace, nullptr, 0);
+    const AcceptPlan ap = plan_accept(s.B, s.N, vocab);
+    const AcceptArgs c = make_accept_args(ap, s.N, vocab, logits, JF_BF16, draft, parent, anc, next_tokens,
+                                          accept_len, accepted_nodes, bonus, accept_workspace);
+    const long accept_grid = (long)s.B * s.N * ap.chunks;
+    fill_counters(p, attn_workspace, stream);
+    return s.D == 128 ? launch_verify_d<128>(p, a, c, accept_grid, stream)
+                      : launch_verify_d<64>(p, a, c, accept_grid, stream);
 }
 
 size_t attention_bf16_workspace_bytes(const jf_attn_shape& s, int max_prefix) {
