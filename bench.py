@@ -4,22 +4,26 @@
 A step is one pass of the whole path over one batch of the budget-16 workload
 (Qwen3-8B attention layer: 32 query / 8 KV heads, head dim 128, bf16, prefix
 2048 in shuffled 16-token pages, a 16-node chain tree):
-    jf_build_ancestor_mask -> jf_tree_attention -> jf_tree_accept (argmax over
-    bf16 target logits [1, 16, 151936], then the acceptance walk).
+    jf_build_ancestor_mask -> jf_tree_verify (tree attention, and the argmax
+    over bf16 target logits [1, 16, 151936] with the acceptance walk, in one
+    launch whose two parts run side by side).
 Each step runs on its own input set; the sets rotate through more than twice
 the 256 MB Infinity Cache so that reads come from HBM. The timed steps are
 replayed from HIP graphs holding one pass over the input sets (every kernel
-still waits for the one before it); `ms_per_step_one_graph_per_step` reports
-the same steps submitted one graph each, host launch cost included. Prints one
-JSON line.
+still waits for the one before it). Also reported: the same steps submitted
+one graph each (host launch cost included), and the same steps with attention
+and acceptance as two launches. Prints one JSON line.
 
 Also measured: each kernel's average duration (HIP events around a graph of
 back-to-back launches of that kernel alone, on the stream it runs on), the
-attention roofline fraction, the budget-256 workload (batch 8, 256-node
-best-first trees, prefixes U[1024, 4096]) as `budget256`, and the fp64 CPU
-oracle on a bounded sample as `cpu_baseline`.
+roofline fraction of the step's dominant kernel (the verification launch) and
+of the attention kernel alone, the budget-256 workload (batch 8, 256-node
+best-first trees, prefixes U[1024, 4096]), budget 16 at streaming size, the
+long-context workload (attention and acceptance apart), ragged budgets with
+the trees' K/V in the paged cache, tree construction, the commit of accepted
+paths, and the fp64 CPU oracle on a bounded sample as `cpu_baseline`.
 
-`roofline.traffic` is the attention kernel's HBM bytes per launch from the
+`roofline.traffic` is the verification kernel's HBM bytes per launch from the
 FETCH_SIZE / WRITE_SIZE counter summary in profiles/ (each counter scaled by
 what it reads for a plain 256 MiB copy in the same run); it is null when the
 kernel sources have changed since those counters were taken. The summary is
@@ -50,6 +54,7 @@ MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 << 20          # counter calibration: plain copy, reads and writes this much
 ATTN_KERNEL = "tree_attn_bf16_kernel"
+STEP_KERNEL = "tree_verify_bf16_kernel"   # attention + acceptance of a budget-16 step, one launch
 
 
 def log(*a):
@@ -76,7 +81,8 @@ def parse():
     return ap.parse_args()
 
 
-ATTN_SOURCES = ("attn_bf16.hip", "jf_common.h")   # the attention kernel, its launch plan and shared helpers
+# the verification kernel: attention (its launch plan), acceptance and shared helpers
+ATTN_SOURCES = ("attn_bf16.hip", "accept_device.h", "jf_common.h")
 
 
 def source_digest():
@@ -93,7 +99,7 @@ def source_digest():
 
 
 def traffic_file(config):
-    return os.path.join(ROOT, "profiles", f"{ATTN_KERNEL}_{config}_hbm_traffic.txt")
+    return os.path.join(ROOT, "profiles", f"{STEP_KERNEL}_{config}_hbm_traffic.txt")
 
 
 def read_counter_csv(d, counter):
@@ -124,7 +130,7 @@ def summarize_pmc(fetch_dir, write_dir, config):
     cf_name, cf = copy_kernel(fetch)
     cw_name, cw = copy_kernel(write)
     f_fac, w_fac = copy_kib / cf, copy_kib / cw
-    lines = [f"# HBM traffic of the tree attention kernel, workload {config}",
+    lines = [f"# HBM traffic of the verification kernel (attention + acceptance), workload {config}",
              "# made by:",
              f"#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
              f"python bench.py --config {config} --profile-steps 20",
@@ -143,9 +149,9 @@ def summarize_pmc(fetch_dir, write_dir, config):
         favg, wavg = sum(fv) / len(fv), sum(wv) / len(wv)
         scaled = favg * f_fac * 1024 + wavg * w_fac * 1024
         lines.append(f"# {name} | {len(fv)} | {favg:.1f} | {wavg:.1f} | {scaled:.0f}")
-        if ATTN_KERNEL in name:
+        if STEP_KERNEL in name:
             attn = (name, scaled)
-    assert attn is not None, "no attention kernel in the counter runs"
+    assert attn is not None, "no verification kernel in the counter runs"
     lines += [f"kernel: {attn[0]}",
               f"traffic_bytes_per_launch: {attn[1]:.0f}",
               f"fetch_factor: {f_fac:.6f}",
@@ -533,16 +539,26 @@ def main():
     t_ver = time_graph(verifies, reps, stream) if verifies else None
     log(f"[bench] per launch: mask {t_mask * 1e3:.2f} us, attention {t_attn * 1e3:.2f} us, "
         f"accept {t_acc * 1e3:.2f} us, verify (attention + accept) {t_ver * 1e3 if t_ver else 0:.2f} us")
-    achieved = nbytes / (t_attn * 1e-3) / 1e9
+    logit_bytes = wl.logits.numel() * wl.logits.element_size() if wl.logits is not None else 0
+    # dominant kernel of the step: the verification launch (attention + acceptance).
+    # Its algorithmic bytes: the attention's, plus the logits read once and the
+    # acceptance outputs (next tokens, accepted nodes, length, bonus)
+    ver_bytes = nbytes + logit_bytes + wl.B * wl.N * 8 + wl.B * 8
+    t_dom = t_ver if t_ver else t_attn
+    dom_bytes = ver_bytes if t_ver else nbytes
+    achieved = dom_bytes / (t_dom * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.config)
     rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
           "frac": round(achieved / HBM_PEAK_GBS, 4),
-          "traffic": None if traffic is None else round(traffic / (t_attn * 1e-3) / 1e9, 1),
+          "traffic": None if traffic is None else round(traffic / (t_dom * 1e-3) / 1e9, 1),
           "traffic_bytes_per_launch": None if traffic is None else int(traffic),
           "traffic_source": traffic_src,
-          "kernel": "tree_attn_bf16_kernel", "algorithmic_bytes": nbytes, "flops": flops,
-          "avg_launch_us": round(t_attn * 1e3, 3)}
-    logit_bytes = wl.logits.numel() * wl.logits.element_size() if wl.logits is not None else 0
+          "kernel": STEP_KERNEL if t_ver else ATTN_KERNEL, "algorithmic_bytes": dom_bytes,
+          "avg_launch_us": round(t_dom * 1e3, 3),
+          "attention_alone": {"kernel": ATTN_KERNEL, "avg_launch_us": round(t_attn * 1e3, 3),
+                              "algorithmic_bytes": nbytes, "flops": flops,
+                              "achieved_GBps": round(nbytes / (t_attn * 1e-3) / 1e9, 1),
+                              "frac": round(nbytes / (t_attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
     result = {
         "metric": "tree-attention tree-tokens/s + % HBM/MFMA roofline at budget 16 and 256",
         "value": round(value, 1),
