@@ -4,15 +4,16 @@
 A step is one pass of the whole path over one batch of the budget-16 workload
 (Qwen3-8B attention layer: 32 query / 8 KV heads, head dim 128, bf16, prefix
 2048 in shuffled 16-token pages, a 16-node chain tree):
-    jf_build_ancestor_mask -> jf_tree_verify (tree attention, and the argmax
-    over bf16 target logits [1, 16, 151936] with the acceptance walk, in one
-    launch whose two parts run side by side).
+    jf_tree_verify: one launch that builds the ancestor bitsets from the parent
+    array, runs the tree attention, and beside it the argmax over bf16 target
+    logits [1, 16, 151936] with the acceptance walk.
 Each step runs on its own input set; the sets rotate through more than twice
 the 256 MB Infinity Cache so that reads come from HBM. The timed steps are
 replayed from HIP graphs holding one pass over the input sets (every kernel
 still waits for the one before it). Also reported: the same steps submitted
-one graph each (host launch cost included), and the same steps with attention
-and acceptance as two launches. Prints one JSON line.
+one graph each (host launch cost included), and the same steps as three
+launches (jf_build_ancestor_mask, jf_tree_attention, jf_tree_accept). Prints
+one JSON line.
 
 Also measured: each kernel's average duration (HIP events around a graph of
 back-to-back launches of that kernel alone, on the stream it runs on), the
@@ -265,18 +266,20 @@ def make_steps(jf, wl, sets, with_accept=True, fused=True):
                                       bonus_token=s.bonus)
 
     def verify(s):
+        # the ancestor bitsets are built inside the call and written to s.anc
         return lambda: jf.tree_verify(s.t["q"], s.t["k_pages"], s.t["v_pages"], s.t["block_table"],
-                                      s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], s.anc, s.t["parent"],
+                                      s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], None, s.t["parent"],
                                       s.t["draft"], s.t["logits"], sm_scale=wl.sm_scale,
                                       max_prefix_len=wl.max_prefix_len, out=s.out, next_tokens=s.nxt,
-                                      accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus)
+                                      accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus,
+                                      anc_out=s.anc)
 
     def step(s):
         m, a = mask(s), attn(s)
         if not with_accept:
             fs = [m, a]
         elif fused and s.t["logits"] is not None:
-            fs = [m, verify(s)]
+            fs = [verify(s)]
         else:
             fs = [m, a, accept(s)]
 
@@ -531,10 +534,11 @@ def main():
     t_attn = time_graph(attns, reps, stream)
     t_acc = time_graph(accepts, reps, stream)
     verifies = [(lambda s=s: jf.tree_verify(s.t["q"], s.t["k_pages"], s.t["v_pages"], s.t["block_table"],
-                                            s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], s.anc, s.t["parent"],
+                                            s.t["prefix_len"], s.t["k_tree"], s.t["v_tree"], None, s.t["parent"],
                                             s.t["draft"], s.t["logits"], sm_scale=wl.sm_scale,
                                             max_prefix_len=wl.max_prefix_len, out=s.out, next_tokens=s.nxt,
-                                            accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus))
+                                            accept_len=s.alen, accepted_nodes=s.nodes, bonus_token=s.bonus,
+                                            anc_out=s.anc))
                 for s in sets] if wl.logits is not None else None
     t_ver = time_graph(verifies, reps, stream) if verifies else None
     log(f"[bench] per launch: mask {t_mask * 1e3:.2f} us, attention {t_attn * 1e3:.2f} us, "
@@ -577,9 +581,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: Qwen3-8B attention layer, batch {wl.B}, {wl.N}-node chain, "
                                f"prefix {wl.max_prefix_len} in shuffled 16-token pages, {wl.Hq}q/{wl.Hkv}kv, "
-                               f"d={wl.D}; step = mask + attention + accept over {wl.vocab}-way bf16 logits"
+                               f"d={wl.D}; step = ancestor bitsets + attention + accept over {wl.vocab}-way bf16 logits"
                                + (" (separate launches)" if args.separate else
-                                  " (jf_tree_verify: attention and acceptance in one launch)"),
+                                  " (jf_tree_verify: bitsets, attention and acceptance in one launch)"),
                    "graph_replay": not args.eager, "steps_per_graph": 1 if args.eager else per,
                    "input_sets": len(sets)},
         "roofline": rl,

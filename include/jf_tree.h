@@ -246,8 +246,18 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
  * attention workspace (size from jf_tree_attention_workspace_bytes), then
  * vocab, target_logits (required) with logits_dtype, draft_tokens, parent,
  * the four acceptance outputs and the acceptance workspace (size from
- * jf_tree_accept_workspace_bytes). Both read the same anc. The results are
- * exactly those of jf_tree_attention followed by jf_tree_accept.
+ * jf_tree_accept_workspace_bytes). The results are exactly those of
+ * jf_tree_attention followed by jf_tree_accept.
+ *
+ *   anc              uint64 [B, N, 4]: with anc_from_parent = 0, the ancestor
+ *                    bitsets (input, from jf_build_ancestor_mask); with
+ *                    anc_from_parent = 1, an output: the call builds the
+ *                    bitsets from parent itself (section 2, tree-causal mask)
+ *                    and writes them here, exactly as jf_build_ancestor_mask
+ *                    writes them (depth and bad_tree are not produced; the
+ *                    tree rules are read the same way, so a broken parent
+ *                    entry counts as a root). Then no separate mask launch is
+ *                    needed before the call.
  *
  * With bf16 attention, bf16 logits and a plan whose attention workgroups
  * have four waves (few query rows per KV head, as at budget 16), both run in
@@ -256,13 +266,13 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab,
  * the rules of its own call (counter region zeroed once, left zero).
  *
  * Host errors: those of jf_tree_attention and of jf_tree_accept, plus
- * JF_ERR_NULL (target_logits NULL) and JF_ERR_WORKSPACE (overlapping
- * workspaces).
+ * JF_ERR_NULL (target_logits NULL), JF_ERR_SHAPE (anc_from_parent not 0 or
+ * 1) and JF_ERR_WORKSPACE (overlapping workspaces).
  */
 jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
                          const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
-                         const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
-                         void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
+                         const void* k_tree, const void* v_tree, uint64_t* anc, int32_t anc_from_parent,
+                         void* out, float* lse, void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
                          const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
                          const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                          int32_t* accepted_nodes, int32_t* bonus_token, void* accept_workspace,

@@ -271,13 +271,14 @@ def test_verify_host_checks(binding):
     p = ctypes.c_void_p(16)
 
     def ver(shape=shape, max_prefix=2048, logits=p, dt=1, V=1000, aws=0x100000, awsb=a_need, cws=0x800000,
-            cwsb=c_need, nul=()):
+            cwsb=c_need, nul=(), from_parent=0):
         a = {n: p for n in ("q", "kp", "vp", "bt", "pl", "kt", "vt", "anc", "out", "draft", "parent", "next",
                             "alen", "nodes", "bonus")}
         for n in nul:
             a[n] = None
         return L.jf_tree_verify(ctypes.byref(shape), max_prefix, a["q"], a["kp"], a["vp"], a["bt"], a["pl"],
-                                a["kt"], a["vt"], a["anc"], a["out"], None, ctypes.c_void_p(aws), awsb, V, logits,
+                                a["kt"], a["vt"], a["anc"], from_parent, a["out"], None, ctypes.c_void_p(aws), awsb,
+                                V, logits,
                                 dt, a["draft"], a["parent"], a["next"], a["alen"], a["nodes"], a["bonus"],
                                 ctypes.c_void_p(cws), cwsb, None)
 
@@ -292,4 +293,7 @@ def test_verify_host_checks(binding):
     assert ver(cwsb=c_need - 1) == JF_ERR_WORKSPACE
     assert ver(cws=0x100000 + a_need - 256) == JF_ERR_WORKSPACE     # overlapping workspaces
     assert ver(aws=0x800000 + 256) == JF_ERR_WORKSPACE
+    assert ver(from_parent=2) == JF_ERR_SHAPE                       # 0: anc is input, 1: built from parent
+    assert ver(from_parent=1, nul=("anc",)) == JF_ERR_NULL          # the built bitsets need somewhere to go
     assert ver(shape=_shape(binding, B=0)) == JF_OK                 # empty batch: no launch
+    assert ver(shape=_shape(binding, B=0), from_parent=1) == JF_OK

@@ -1,8 +1,10 @@
 """GPU parity of jf_tree_verify (attention and acceptance in one call, through
 the C ABI): bit-identical to jf_tree_attention followed by jf_tree_accept on
 the same inputs, in the fused one-launch form and in the two-launch fallback,
+with the ancestor bitsets given or built from the parent array inside the
+call (then bit-identical to jf_build_ancestor_mask's, broken trees included),
 and checked against the fp64 oracle (attention to the bf16 bar of 1e-2 and
-1e-2 * max|ref|, or 1e-5 for fp32; acceptance bit-exact)."""
+1e-2 * max|ref|, or 1e-5 for fp32; acceptance and bitsets bit-exact)."""
 
 import numpy as np
 import pytest
@@ -38,6 +40,7 @@ def _separate(jf, wl, d, anc):
 
 
 def _verify(jf, wl, d, anc):
+    # anc None: the call builds the bitsets from the parent array
     return jf.tree_verify(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["prefix_len"], d["k_tree"],
                           d["v_tree"], anc, d["parent"], d["draft"], d["logits"], sm_scale=wl.sm_scale,
                           max_prefix_len=wl.max_prefix_len, return_lse=True)
@@ -47,13 +50,16 @@ def _check(jf, wl, what, tol=1e-2):
     d = _dev(wl)
     anc, _, _ = jf.build_ancestor_mask(d["parent"])
     ref = _separate(jf, wl, d, anc)
-    got = _verify(jf, wl, d, anc)
-    torch.cuda.synchronize()
     itype = torch.int16 if wl.dtype == torch.bfloat16 else torch.int32
-    assert torch.equal(got[0].view(itype), ref[0].view(itype)), what
-    assert torch.equal(got[1].view(torch.int32), ref[1].view(torch.int32)), what
-    for g, r in zip(got[2:], ref[2:]):
-        assert torch.equal(g, r), what
+    for given in (True, False):
+        got = _verify(jf, wl, d, anc if given else None)
+        torch.cuda.synchronize()
+        how = f"{what} ({'bitsets given' if given else 'bitsets built in the call'})"
+        assert torch.equal(got[0].view(itype), ref[0].view(itype)), how
+        assert torch.equal(got[1].view(torch.int32), ref[1].view(torch.int32)), how
+        for g, r in zip(got[2:6], ref[2:]):
+            assert torch.equal(g, r), how
+        assert torch.equal(got[6], anc), how
     # against the oracle
     o, l = oracle.tree_attention(wl.q, wl.k_pages, wl.v_pages, wl.block_table, wl.prefix_len, wl.k_tree, wl.v_tree,
                                  wl.parent, wl.sm_scale)
@@ -93,6 +99,37 @@ def test_verify_four_wave_row_pairs(jf, monkeypatch):
     _check(jf, wl, "rpw2_fused")
 
 
+def test_verify_builds_bitsets_of_deep_and_broken_trees(jf, monkeypatch):
+    # one launch with the bitsets built in the call: a 256-node chain (eight
+    # doubling rounds) and star as four-wave 256-row blocks, and trees with broken
+    # parent entries, which both the call and jf_build_ancestor_mask read as roots
+    monkeypatch.setenv("JF_RPW", "2")
+    for tree, B in ((W.tree_chain(256), 1), (np.array([-1] + [0] * 255, dtype=np.int32), 1)):
+        wl = W.make_workload("c1_chain16", 13, B=B, N=256, prefix=("list", [300]), Hq=2, Hkv=2, accept=LOGITS)
+        wl.parent = torch.from_numpy(np.stack([tree] * B))
+        _check(jf, wl, f"256 nodes, depth {int(oracle.build_ancestor_mask(wl.parent.numpy())[1].max())}")
+    monkeypatch.delenv("JF_RPW")
+    wl = W.make_workload("c1_chain16", 14, B=4, N=24, prefix=("list", [150, 0, 37, 400]), Hq=8, Hkv=2,
+                         tree=("random", 6), accept=LOGITS)
+    par = wl.parent.numpy().copy()
+    par[0, 0] = 3            # the root has a parent
+    par[1, 5] = 7            # a parent after its child
+    par[2, 9] = -4           # out of range
+    par[3, 11] = 11          # its own parent
+    d = _dev(wl)
+    d["parent"] = torch.from_numpy(par).to(DEV)
+    anc, _, bad = jf.build_ancestor_mask(d["parent"])
+    assert bad.cpu().tolist() == [1, 1, 1, 1]
+    ref = _separate(jf, wl, d, anc)
+    got = _verify(jf, wl, d, None)
+    torch.cuda.synchronize()
+    assert torch.equal(got[6], anc)
+    assert torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16))
+    for g, r in zip(got[2:6], ref[2:]):
+        assert torch.equal(g, r)
+    print("  broken trees: bitsets and results identical to the mask kernel's reading", flush=True)
+
+
 def test_verify_fp32_fallback(jf):
     wl = W.make_workload("c0_tiny_fp32", 2, accept=("logits", 3000, 3.0, 0.7))
     _check(jf, wl, "fp32", tol=1e-5)
@@ -102,7 +139,7 @@ def test_verify_graph_replay(jf):
     wl = W.make_workload("c1_chain16", 12, accept=LOGITS)
     d = _dev(wl)
     anc, _, _ = jf.build_ancestor_mask(d["parent"])
-    ref = [t.clone() for t in _verify(jf, wl, d, anc) if t is not None]
+    ref = [t.clone() for t in _verify(jf, wl, d, anc)[:6] if t is not None]
     torch.cuda.synchronize()
     bufs = dict(out=torch.empty_like(d["q"]), lse=torch.empty(d["q"].shape[:3], dtype=torch.float32, device=DEV),
                 alen=torch.empty((wl.B,), dtype=torch.int32, device=DEV),
@@ -110,11 +147,15 @@ def test_verify_graph_replay(jf):
                 bonus=torch.empty((wl.B,), dtype=torch.int32, device=DEV),
                 nxt=torch.empty((wl.B, wl.N), dtype=torch.int32, device=DEV))
 
+    anc_built = torch.empty_like(anc)
+
     def call():
+        # bitsets built inside the call (written to anc_built)
         jf.tree_verify(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["prefix_len"], d["k_tree"],
-                       d["v_tree"], anc, d["parent"], d["draft"], d["logits"], sm_scale=wl.sm_scale,
+                       d["v_tree"], None, d["parent"], d["draft"], d["logits"], sm_scale=wl.sm_scale,
                        max_prefix_len=wl.max_prefix_len, out=bufs["out"], lse=bufs["lse"], accept_len=bufs["alen"],
-                       accepted_nodes=bufs["nodes"], bonus_token=bufs["bonus"], next_tokens=bufs["nxt"])
+                       accepted_nodes=bufs["nodes"], bonus_token=bufs["bonus"], next_tokens=bufs["nxt"],
+                       anc_out=anc_built)
 
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
@@ -130,5 +171,7 @@ def test_verify_graph_replay(jf):
         assert torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16)), rep
         for a, b in zip(got[1:], ref[1:]):
             assert torch.equal(a, b), rep
+        assert torch.equal(anc_built, anc), rep
+        anc_built.zero_()
         _verify(jf, wl, d, anc)                        # eager work between replays
         torch.cuda.synchronize()

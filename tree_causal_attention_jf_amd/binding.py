@@ -86,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_accept.restype = i32
     lib.jf_tree_accept.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.jf_tree_verify.restype = i32
-    lib.jf_tree_verify.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    lib.jf_tree_verify.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                    vp, sz, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.jf_tree_attention_paged_tree.restype = i32
     lib.jf_tree_attention_paged_tree.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -309,18 +309,25 @@ def tree_verify(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, an
                 sm_scale: Optional[float] = None, max_prefix_len: Optional[int] = None,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, return_lse: bool = False,
                 next_tokens=None, accept_len=None, accepted_nodes=None, bonus_token=None,
-                attn_workspace: Optional[torch.Tensor] = None, accept_workspace: Optional[torch.Tensor] = None):
+                attn_workspace: Optional[torch.Tensor] = None, accept_workspace: Optional[torch.Tensor] = None,
+                anc_out: Optional[torch.Tensor] = None):
     """One verification step: tree attention and acceptance over the target logits
-    (see include/jf_tree.h). Returns (out, lse or None, accept_len, accepted_nodes,
-    bonus_token, next_tokens)."""
+    (see include/jf_tree.h). `anc` is the ancestor bitset from build_ancestor_mask,
+    or None: the call then builds it from `parent` itself (into `anc_out`, allocated
+    when None). Returns (out, lse or None, accept_len, accepted_nodes, bonus_token,
+    next_tokens, anc)."""
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (k_tree, "k_tree"), (v_tree, "v_tree")):
         _need(t, n, q.dtype)
     _need(block_table, "block_table", torch.int32)
     _need(prefix_len, "prefix_len", torch.int32)
-    _need(anc, "anc", torch.uint64)
     _need(parent, "parent", torch.int32)
     _need(draft, "draft", torch.int32)
     _need(logits, "logits")
+    from_parent = anc is None
+    if from_parent:
+        anc = anc_out if anc_out is not None else torch.empty((*parent.shape, 4), dtype=torch.uint64,
+                                                              device=parent.device)
+    _need(anc, "anc", torch.uint64)
     ldt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}[logits.dtype]
     shape = attn_shape(q, k_pages, block_table, sm_scale)
     if max_prefix_len is None:
@@ -347,12 +354,12 @@ def tree_verify(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, an
         _default_ws.get(dev, "accept", tree_accept_workspace_bytes(B, N, vocab))
     cws_bytes = cws.numel() * cws.element_size()
     st = _lib.jf_tree_verify(ctypes.byref(shape), int(max_prefix_len), _ptr(q), _ptr(k_pages), _ptr(v_pages),
-                             _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(out),
-                             _ptr(lse), _ptr(aws), aws_bytes, vocab, _ptr(logits), ldt, _ptr(draft), _ptr(parent),
+                             _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(anc),
+                             1 if from_parent else 0, _ptr(out), _ptr(lse), _ptr(aws), aws_bytes, vocab, _ptr(logits), ldt, _ptr(draft), _ptr(parent),
                              _ptr(next_tokens), _ptr(accept_len), _ptr(accepted_nodes), _ptr(bonus_token),
                              _ptr(cws), cws_bytes, _stream(dev))
     _check("jf_tree_verify", st)
-    return out, lse, accept_len, accepted_nodes, bonus_token, next_tokens
+    return out, lse, accept_len, accepted_nodes, bonus_token, next_tokens, anc
 
 
 def commit_accepted(k_tree, v_tree, accept_len, accepted_nodes, block_table, prefix_len, k_pages, v_pages,

@@ -96,6 +96,7 @@ AcceptArgs make_accept_args(const AcceptPlan& p, int N, int vocab, const void* l
     a.chunk_len = p.chunk_len;
     const size_t elt = dtype == JF_BF16 ? 2 : 4;
     a.aligned = ((reinterpret_cast<uintptr_t>(logits) % 16) == 0) && (((size_t)vocab * elt) % 16 == 0);
+    a.anc_out = nullptr;
     return a;
 }
 

@@ -152,8 +152,10 @@ __device__ __forceinline__ NodeIn load_node(int b, int N, const int32_t* __restr
         const size_t r = (size_t)b * N + u;
         n.p = parent[r];
         n.d = draft[r];
-        #pragma unroll
-        for (int k = 0; k < kAncWords; ++k) n.a[k] = anc[r * kAncWords + k];
+        if (anc) {
+            #pragma unroll
+            for (int k = 0; k < kAncWords; ++k) n.a[k] = anc[r * kAncWords + k];
+        }
     }
     return n;
 }
@@ -275,6 +277,7 @@ struct AcceptArgs {
     uint64_t* partial;  // [B*N*C]   chunk winners as keys (workspace)
     int N, vocab, chunks, chunk_len;
     int groups;         // arrival groups per sequence (1: every workgroup arrives on seq_count)
+    uint64_t* anc_out;  // non-null: the walk builds the ancestor sets from parent (anc unused) and writes them here
     int aligned;        // rows start on 16-byte boundaries and chunk_len keeps them there
 };
 
@@ -331,7 +334,7 @@ __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk)
 
     // every load of the final phase at once: this thread's node and up to 4
     // chunk keys per pass (one pass covers N * C <= 1024)
-    const NodeIn nd = load_node(b, a.N, a.parent, a.draft, a.anc);
+    NodeIn nd = load_node(b, a.N, a.parent, a.draft, a.anc_out ? nullptr : a.anc);
     const uint64_t* pk = a.partial + (size_t)b * per_seq;
     const int u = threadIdx.x;
     if (u < a.N) s_key[u] = 0ull;
@@ -356,6 +359,17 @@ __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk)
         a.next_tokens[(size_t)b * a.N + u] = nx;
     }
     __syncthreads();
+    if (a.anc_out) {
+        // the ancestor sets from the parent array (pointer doubling in LDS), written out as well
+        const auto sets = tree_sets_lds(nd.p, a.N);
+        if (u < a.N) {
+            #pragma unroll
+            for (int k = 0; k < kAncWords; ++k) {
+                nd.a[k] = sets[u][k];
+                a.anc_out[((size_t)b * a.N + u) * kAncWords + k] = nd.a[k];
+            }
+        }
+    }
     walk_sequence(b, a.N, nd.p, nd.d, nd.a, s_next, a.accept_len, a.accepted_nodes, a.bonus);
 }
 

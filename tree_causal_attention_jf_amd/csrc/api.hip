@@ -29,7 +29,7 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                               void* attn_workspace, int vocab, const void* logits, const int32_t* draft,
                               const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                               int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
-                              hipStream_t stream);
+                              int anc_from_parent, hipStream_t stream);
 bool verify_fusable(const jf_attn_shape& s, int max_prefix, int logits_dtype);
 hipError_t launch_commit(const jf_attn_shape& s, const void* k_tree, const void* v_tree, const int32_t* accept_len,
                          const int32_t* accepted_nodes, const int32_t* block_table, const int32_t* prefix_len,
@@ -203,8 +203,8 @@ jf_status jf_tree_accept(int32_t B, int32_t N, int32_t vocab, const void* target
 
 jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const void* q, const void* k_pages,
                          const void* v_pages, const int32_t* block_table, const int32_t* prefix_len,
-                         const void* k_tree, const void* v_tree, const uint64_t* anc, void* out, float* lse,
-                         void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
+                         const void* k_tree, const void* v_tree, uint64_t* anc, int32_t anc_from_parent,
+                         void* out, float* lse, void* attn_workspace, size_t attn_workspace_bytes, int32_t vocab,
                          const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
                          const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                          int32_t* accepted_nodes, int32_t* bonus_token, void* accept_workspace,
@@ -213,6 +213,7 @@ jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const v
                                         v_tree, anc, out, attn_workspace, attn_workspace_bytes);
     if (st != JF_OK) return st;
     if (!target_logits) return JF_ERR_NULL;
+    if (anc_from_parent != 0 && anc_from_parent != 1) return JF_ERR_SHAPE;
     st = check_accept_call(s->B, s->N, vocab, target_logits, logits_dtype, nullptr, draft_tokens, parent, anc,
                            next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace,
                            accept_workspace_bytes);
@@ -229,9 +230,13 @@ jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const v
     if (jf::verify_fusable(*s, max_prefix_len, logits_dtype)) {
         e = jf::launch_verify_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree,
                                    anc, out, lse, attn_workspace, vocab, target_logits, draft_tokens, parent,
-                                   next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace, stream);
+                                   next_tokens, accept_len, accepted_nodes, bonus_token, accept_workspace,
+                                   anc_from_parent, stream);
     } else {
-        e = s->dtype == JF_BF16
+        e = anc_from_parent ? jf::launch_ancestor_mask(parent, s->B, s->N, anc, nullptr, nullptr, stream)
+                            : hipSuccess;
+        if (e == hipSuccess)
+            e = s->dtype == JF_BF16
                 ? jf::launch_attention_bf16(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,
                                             k_tree, v_tree, anc, out, lse, attn_workspace, stream)
                 : jf::launch_attention_f32(*s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len,

@@ -72,6 +72,7 @@ struct AttnArgs {
     const uint16_t* kt;
     const uint16_t* vt;
     const uint64_t* anc;
+    const int32_t* parent_sets;   // non-null: tree WGs build the ancestor words from this parent array
     uint16_t* out;
     float* lse;
     int* counters;     // [items]                       zero between calls
@@ -581,6 +582,10 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     const int p_avail = tree_wg ? 0 : min(pps, a.max_pages - p_begin);
     int L = a.prefix_len[b];
     int nb = a.tree_len ? a.tree_len[b] : a.N;
+    // when this launch builds the ancestor words itself: the parent of node `lane`
+    // (trees of at most 64 nodes: every wave builds them alone) or of node tid
+    const int par_idx = a.N <= kWave ? lane : tid;
+    const int par_own = (a.parent_sets && par_idx < a.N) ? a.parent_sets[(long)b * a.N + par_idx] : -1;
     int pid[PPT];
     #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -636,6 +641,26 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     const int p_end = tree_wg ? 0 : min(npages, p_begin + pps);
     const int tok_begin = p_begin * kPage;
     const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
+    if (a.parent_sets && has_tree) {
+        // the ancestor words come from the parent array (the loads above read a
+        // buffer this launch writes, and are discarded): pointer doubling in LDS
+        if (a.N <= kWave) {
+            const uint64_t set = tree_set_wave(par_own, a.N);
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk) {
+                const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)set, node[blk]);
+                const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(set >> 32), node[blk]);
+                ancw[blk] = u64x4{row_ok[blk] ? (((uint64_t)hi << 32) | lo) : 0ull, 0, 0, 0};
+            }
+        } else {
+            const auto sets = tree_sets_lds(par_own, a.N);
+            #pragma unroll
+            for (int blk = 0; blk < RPW; ++blk) {
+                #pragma unroll
+                for (int k = 0; k < kAncWords; ++k) ancw[blk][k] = row_ok[blk] ? sets[node[blk]][k] : 0ull;
+            }
+        }
+    }
     if (!has_tree) {
         #pragma unroll
         for (int blk = 0; blk < RPW; ++blk) ancw[blk] = u64x4{0, 0, 0, 0};
@@ -1190,6 +1215,7 @@ static AttnArgs make_attn_args(const AttnPlanBf16& p, const jf_attn_shape& s, in
     a.kt = static_cast<const uint16_t*>(k_tree);
     a.vt = static_cast<const uint16_t*>(v_tree);
     a.anc = anc;
+    a.parent_sets = nullptr;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     char* ws = static_cast<char*>(workspace);
@@ -1292,13 +1318,19 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                               void* attn_workspace, int vocab, const void* logits, const int32_t* draft,
                               const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                               int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
-                              hipStream_t stream) {
+                              int anc_from_parent, hipStream_t stream) {
     const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
-    const AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
-                                      v_tree, anc, out, lse, attn_workspace, nullptr, 0);
+    AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                v_tree, anc, out, lse, attn_workspace, nullptr, 0);
     const AcceptPlan ap = plan_accept(s.B, s.N, vocab);
-    const AcceptArgs c = make_accept_args(ap, s.N, vocab, logits, JF_BF16, draft, parent, anc, next_tokens,
-                                          accept_len, accepted_nodes, bonus, accept_workspace);
+    AcceptArgs c = make_accept_args(ap, s.N, vocab, logits, JF_BF16, draft, parent, anc, next_tokens,
+                                    accept_len, accepted_nodes, bonus, accept_workspace);
+    if (anc_from_parent) {
+        // both parts build the ancestor sets from parent in LDS; the acceptance part
+        // also writes them to anc
+        a.parent_sets = parent;
+        c.anc_out = const_cast<uint64_t*>(anc);
+    }
     const long accept_grid = (long)s.B * s.N * ap.chunks;
     fill_counters(p, attn_workspace, stream);
     return s.D == 128 ? launch_verify_d<128>(p, a, c, accept_grid, stream)

@@ -46,6 +46,76 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// Ancestor-or-self sets of one tree (N <= 256 nodes, 256 bits each) from its
+// parent array, in LDS, by pointer doubling: after round k node i holds every
+// node within distance < 2^k above it and a pointer to its 2^k-th ancestor, so
+// at most 8 rounds cover any tree. A parent entry that breaks the tree rules
+// (parent[0] != -1, or parent[i] outside [0, i)) is read as -1, a root, as
+// jf_build_ancestor_mask reads it. One thread per node: the workgroup has at
+// least N threads, every thread calls this (it holds barriers), and thread i
+// passes parent[i] (loaded early by the caller, so its latency hides behind
+// other loads; any value for i >= N). Returns the LDS array of sets, complete
+// for nodes < N when the call returns.
+__device__ __forceinline__ const uint64_t (*tree_sets_lds(int p, int N))[kAncWords] {
+    __shared__ uint64_t s_set[JF_MAX_NODES][kAncWords];
+    __shared__ int16_t s_up[JF_MAX_NODES];
+    const int i = threadIdx.x;
+    const bool mine = i < N;
+    if (mine) {
+        if (!((i == 0) ? (p == -1) : (p >= 0 && p < i))) p = -1;
+        #pragma unroll
+        for (int w = 0; w < kAncWords; ++w) s_set[i][w] = (w == (i >> 6)) ? (1ull << (i & 63)) : 0ull;
+        s_up[i] = (int16_t)p;
+    }
+    __syncthreads();
+    for (int round = 0; round < 8; ++round) {
+        uint64_t v[kAncWords];
+        int jj = -1;
+        if (mine) {
+            const int j = s_up[i];
+            #pragma unroll
+            for (int w = 0; w < kAncWords; ++w) v[w] = s_set[i][w];
+            if (j >= 0) {
+                #pragma unroll
+                for (int w = 0; w < kAncWords; ++w) v[w] |= s_set[j][w];
+                jj = s_up[j];
+            }
+        }
+        __syncthreads();                                   // every read of this round before any write
+        if (mine) {
+            #pragma unroll
+            for (int w = 0; w < kAncWords; ++w) s_set[i][w] = v[w];
+            s_up[i] = (int16_t)jj;
+        }
+        if (!__syncthreads_or(mine && jj >= 0)) break;
+    }
+    return s_set;
+}
+
+// The same for trees of at most 64 nodes, inside one wave: lane l < N ends with
+// node l's set (bits 0..63), by pointer doubling across the lanes with
+// shuffles, so no LDS and no barrier; every wave may run it on its own. p is
+// parent[lane] (any value for lanes >= N). At most 7 rounds: a pointer only
+// moves up, and its distance doubles each round.
+__device__ __forceinline__ uint64_t tree_set_wave(int p, int N) {
+    const int l = threadIdx.x & 63;
+    const bool mine = l < N;
+    if (!mine || !((l == 0) ? (p == -1) : (p >= 0 && p < l))) p = -1;
+    uint64_t set = mine ? (1ull << l) : 0ull;
+    int up = p;
+    for (int round = 0; round < 7 && __any(up >= 0); ++round) {
+        const int j = up >= 0 ? up : l;
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)set, j);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(set >> 32), j);
+        const int uj = __shfl(up, j);
+        if (up >= 0) {
+            set |= ((uint64_t)hi << 32) | lo;
+            up = uj;
+        }
+    }
+    return set;
+}
+
 // Workgroup id -> logical id such that each XCD receives one contiguous range
 // of logical ids (hardware deals workgroup x to XCD x % 8).
 __device__ __forceinline__ int xcd_remap(int x, int total) {
