@@ -640,6 +640,31 @@ def main():
         log(f"[bench] budget16 streaming: {t5 * 1e3:.1f} us, {gbs5:.0f} GB/s")
         del b5, m5, a5
 
+    # ---- the draft head's pass: one sequence, a 256-node tree, an 8192-token draft cache
+    if not args.no_budget256:
+        log("[bench] building workload draft_head_b1")
+        wl6 = W.make_workload("draft_head_b1", 0, with_accept=False)
+        b6 = DeviceSet(wl6)
+        sets6 = rotation_sets(wl6, b6, cap=16)
+        m6, a6, _, _ = make_steps(jf, wl6, sets6, with_accept=False)
+        with torch.cuda.stream(stream):
+            for f in m6 + a6:
+                f()
+        torch.cuda.synchronize()
+        nb6, fl6 = attention_work(wl6, b6.depth.cpu().numpy())
+        t6 = time_graph(a6, max(4, 400 // len(sets6)), stream)
+        tf6 = fl6 / (t6 * 1e-3) / 1e12
+        result["draft_head_pass"] = {
+            "workload": "draft_head_b1: the draft layer's tree-causal pass, batch 1, 256-node best-first tree, "
+                        "8192-token cache, 32q/8kv, d=128",
+            "tree_tokens_per_s": round(wl6.B * wl6.N / (t6 * 1e-3), 1), "attention_us": round(t6 * 1e3, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf6, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "hbm_GBps": round(nb6 / (t6 * 1e-3) / 1e9, 1), "flops": fl6, "algorithmic_bytes": nb6},
+            "input_sets": len(sets6)}
+        log(f"[bench] draft head pass: {t6 * 1e3:.1f} us, {tf6:.1f} TFLOP/s")
+        del sets6, b6, m6, a6
+
     # ---- long context: batch 4, prefix 32768, 256-node trees; attention and acceptance timed apart
     if not args.no_long_context:
         log("[bench] building workload c4_bf256_32k")

@@ -338,7 +338,7 @@ def _sampled_rows(wl, count, seed):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["c2_bf256_b8", "c3_bf64_b32", "c4_bf256_32k"])
+@pytest.mark.parametrize("name", ["c2_bf256_b8", "c3_bf64_b32", "c4_bf256_32k", "draft_head_b1"])
 def test_attention_bf16_large_sampled(jf, name):
     for unscaled in (False, True):
         wl = W.make_workload(name, 0, with_accept=False, unscaled=unscaled)

@@ -316,6 +316,11 @@ CONFIGS = {
     "c3_bf64_b32": dict(dtype=torch.bfloat16, B=32, prefix=("uniform", 512, 8192), N=64, Hq=32, Hkv=4,
                         D=128, tree=("best_first", 4, 10, 2.0), data_scale=1.0 / math.sqrt(128.0),
                         accept=("ids", QWEN3_VOCAB, 0.8)),
+    # the draft head's own tree-causal pass: one decoder layer in the target's attention shape, all 256
+    # nodes of one sequence's tree in one call over its KV cache of the fused target features (8192 tokens)
+    "draft_head_b1": dict(dtype=torch.bfloat16, B=1, prefix=("fixed", 8192), N=256, Hq=32, Hkv=8, D=128,
+                          tree=("best_first", 4, 12, 2.0), data_scale=1.0 / math.sqrt(128.0),
+                          accept=("ids", QWEN3_VOCAB, 0.8)),
     # long-context verification, batch 4, prefix 32768, budget 256, acceptance over full logits
     "c4_bf256_32k": dict(dtype=torch.bfloat16, B=4, prefix=("fixed", 32768), N=256, Hq=32, Hkv=8, D=128,
                          tree=("best_first", 4, 12, 2.0), data_scale=1.0 / math.sqrt(128.0),
