@@ -86,6 +86,8 @@ LOGITS = ("logits", 20000, 3.0, 0.8)
     ("d64_unaligned_vocab", dict(B=2, N=16, prefix=("list", [300, 90]), Hq=8, Hkv=2, D=64, tree=("random", 5),
                                  accept=("logits", 4099, 3.0, 0.8))),              # rows not 16-byte aligned
     ("fallback_256_rows", dict(B=2, N=64, prefix=("list", [700, 1300]), tree=("random", 8), accept=LOGITS)),
+    ("one_node_trees", dict(B=3, N=1, prefix=("list", [0, 33, 512]), accept=LOGITS)),       # root only
+    ("empty_prefixes", dict(B=2, N=20, prefix=("list", [0, 0]), Hq=8, Hkv=2, tree=("random", 7), accept=LOGITS)),
 ])
 def test_verify_matches_separate_calls_and_oracle(jf, name, kw):
     wl = W.make_workload("c1_chain16", 9, **kw)
