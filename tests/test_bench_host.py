@@ -1,0 +1,52 @@
+"""Host logic of bench.py that needs no GPU: the counter summary (traffic from
+FETCH_SIZE / WRITE_SIZE, scaled by what a plain copy of known size reads), its
+staleness check against the kernel sources, and the refusal of more than one GPU."""
+
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+VERIFY = "void jf::tree_verify_bf16_kernel<128, 1, 4, 1>(jf::AttnArgs, jf::AcceptArgs, unsigned int)"
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_summary_scales_counters_by_the_copy_and_detects_stale_sources(tmp_path, monkeypatch):
+    copy_kib = bench.COPY_BYTES / 1024
+    # the copy's read shows as half its size (factor 2), its write in full (factor 1)
+    _write_counters(tmp_path / "F", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", copy_kib / 2),
+                                                    (VERIFY, 100.0), (VERIFY, 300.0)])
+    _write_counters(tmp_path / "W", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib),
+                                                    (VERIFY, 10.0), (VERIFY, 30.0)])
+    out = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "traffic_file", lambda config: str(out))
+    bench.summarize_pmc(str(tmp_path / "F"), str(tmp_path / "W"), "c1_chain16")
+    traffic, src = bench.read_traffic("c1_chain16")
+    # average fetch 200 KiB x 2 + average write 20 KiB x 1
+    assert traffic == pytest.approx((200 * 2 + 20) * 1024, rel=1e-6)
+    assert src == os.path.relpath(str(out), ROOT)
+    # a change to the kernel's sources makes the summary stale
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 64)
+    assert bench.read_traffic("c1_chain16") == (None, "kernel sources changed since the counters were taken")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], stdout=subprocess.PIPE,
+                       stderr=subprocess.PIPE, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
