@@ -392,9 +392,18 @@ def rotation_sets(wl, base, budget_bytes=2 * MALL_BYTES, cap=64):
     return [base] + [DeviceSet(wl, src=base) for _ in range(n - 1)]
 
 
-def cpu_baseline(wl, seconds):
+def cpu_baseline(wl, seconds, threads_limit=None):
+    """The oracle on full steps of the workload for about `seconds`; with
+    threads_limit, its BLAS pools are held to that many threads."""
+    import contextlib
+
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with (threadpool_limits(threads_limit) if threads_limit else contextlib.nullcontext()):
+        return _cpu_baseline(oracle, wl, seconds, threadpool_info)
+
+
+def _cpu_baseline(oracle, wl, seconds, threadpool_info):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     steps = 0
     t0 = time.perf_counter()
@@ -719,6 +728,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline_single_thread"] = cpu_baseline(wl, args.cpu_seconds / 2, threads_limit=1)
     print(json.dumps(result), flush=True)
 
 
