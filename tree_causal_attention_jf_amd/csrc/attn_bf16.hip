@@ -51,6 +51,11 @@
 // In the matrix-core output layout each lane owns one query row and 16 keys
 // per 32-key block, so the 256-bit ancestor bitset of that row's node sits in
 // the lane's registers and masking is a per-register bit test.
+//
+// The same body also runs inside the verification launch (tree_verify_bf16_kernel
+// below): attention workgroups first, then the acceptance workgroups (argmax over
+// the target logits and the walk) in the same grid. There the workgroups that run
+// tree tiles may build the ancestor bitsets from the parent array themselves.
 #include "jf_common.h"
 #include "accept_device.h"
 
@@ -643,7 +648,8 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
     if (a.parent_sets && has_tree) {
         // the ancestor words come from the parent array (the loads above read a
-        // buffer this launch writes, and are discarded): pointer doubling in LDS
+        // buffer this launch writes, and are discarded): pointer doubling across the
+        // wave's lanes for trees of at most 64 nodes, else in LDS
         if (a.N <= kWave) {
             const uint64_t set = tree_set_wave(par_own, a.N);
             #pragma unroll
@@ -1329,8 +1335,8 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
     AcceptArgs c = make_accept_args(ap, s.N, vocab, logits, JF_BF16, draft, parent, anc, next_tokens,
                                     accept_len, accepted_nodes, bonus, accept_workspace);
     if (anc_from_parent) {
-        // both parts build the ancestor sets from parent in LDS; the acceptance part
-        // also writes them to anc
+        // both parts build the ancestor sets from parent themselves; the acceptance
+        // part also writes them to anc
         a.parent_sets = parent;
         c.anc_out = const_cast<uint64_t*>(anc);
     }
