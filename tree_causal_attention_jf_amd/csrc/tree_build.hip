@@ -190,7 +190,8 @@ __device__ __forceinline__ K wave_max_key(K v) {
 // Run by wave 0 alone.
 template <int KT>
 __device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
-                          const int* s_cnt) {
+                          const int* s_cnt, int n0 = 0, const double* s_nsc = nullptr, const int* s_dep = nullptr,
+                          const int* s_r = nullptr) {
     const int lane = threadIdx.x;
     const int N = a.N;
     int32_t* par = a.parent + (size_t)b * N;
@@ -213,7 +214,24 @@ __device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, cons
         hc[s] = (v < rows_live) ? s_cnt[v] : 0;
     }
     int n = 0;
-    if (nb >= 1) {
+    if (n0 > 0) {
+        // continue from nodes 0 .. n0-1 already grown (their scores, depths and
+        // next child ranks in LDS; their outputs already written)
+        #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int v = s * 64 + lane;
+            if (v < n0) {
+                hs[s] = s_nsc[v];
+                hd[s] = s_dep[v];
+                hr[s] = s_r[v];
+                if (hd[s] < a.cap && hr[s] < hc[s]) {
+                    hv[s] = hs[s] + s_lp[v * KT + hr[s]];
+                    hn[s] = hr[s] + 1 < hc[s] ? s_lp[v * KT + hr[s] + 1] : ninf;
+                }
+            }
+        }
+        n = n0;
+    } else if (nb >= 1) {
         if (lane == 0) {
             par[0] = -1;
             tok[0] = -1;
@@ -299,6 +317,142 @@ __device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, cons
     if (lane == 0) a.tree_len[b] = (nb >= 0 && nb <= N) ? n : -1;
 }
 
+// ---------------------------------------------------------------- growth in batches
+
+// Exclusive prefix sum of x over the workgroup (kBuildThreads threads); *total
+// receives the sum. Holds barriers: every thread calls it.
+__device__ __forceinline__ int block_exclusive_sum(int x, int* s_tmp, int* total) {
+    const int t = threadIdx.x;
+    s_tmp[t] = x;
+    __syncthreads();
+    for (int off = 1; off < kBuildThreads; off <<= 1) {
+        const int y = t >= off ? s_tmp[t - off] : 0;
+        __syncthreads();
+        s_tmp[t] += y;
+        __syncthreads();
+    }
+    const int incl = s_tmp[t];
+    *total = s_tmp[kBuildThreads - 1];
+    __syncthreads();
+    return incl - x;
+}
+
+// Exclusive prefix maximum of x over the workgroup (-inf for thread 0).
+__device__ __forceinline__ double block_exclusive_max(double x, double* s_tmp) {
+    const int t = threadIdx.x;
+    s_tmp[t] = x;
+    __syncthreads();
+    for (int off = 1; off < kBuildThreads; off <<= 1) {
+        const double y = t >= off ? s_tmp[t - off] : -__builtin_inf();
+        __syncthreads();
+        s_tmp[t] = s_tmp[t] > y ? s_tmp[t] : y;
+        __syncthreads();
+    }
+    const double excl = t > 0 ? s_tmp[t - 1] : -__builtin_inf();
+    __syncthreads();
+    return excl;
+}
+
+// Scores only fall along a path (log-probabilities are negative), so the serial
+// best-first loop can be run many steps at a time: with every child not yet taken
+// of every grown node sorted by the loop's own order (score, then the parent that
+// joined first, then the child's rank), the loop takes c_1, c_2, ... in that order
+// for as long as each c_i scores at least as well as the best child of the nodes
+// c_1 .. c_{i-1} have just become (a new node joins after every existing parent, so
+// on equal scores c_i still wins). One round sorts the candidates (bitonic, in LDS),
+// finds that prefix and grows it. Rounds go on while they add at least 4 nodes;
+// the serial loop then continues from the state left in LDS. Run by the whole
+// workgroup. Returns the nodes grown (>= 1 when nb >= 1).
+template <int KT>
+__device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
+                            const int* s_cnt, double* s_nsc, int* s_dep, int* s_r, double* c_sc, int* c_key,
+                            double* s_dtmp, int* s_itmp) {
+    const int t = threadIdx.x;
+    const int N = a.N;
+    int32_t* par = a.parent + (size_t)b * N;
+    int32_t* tok = a.token + (size_t)b * N;
+    double* sc = a.score ? a.score + (size_t)b * N : nullptr;
+    const double ninf = -__builtin_inf();
+    if (nb < 1) return 0;
+    if (t == 0) {
+        par[0] = -1;
+        tok[0] = -1;
+        if (sc) sc[0] = 0.0;
+        s_nsc[0] = 0.0;
+        s_dep[0] = 1;
+    }
+    if (t < JF_MAX_NODES) s_r[t] = 0;
+    __syncthreads();
+    int n = 1;
+    while (n < nb) {
+        // candidates: node t (grown, expandable) offers its children r .. cnt-1
+        int cnt_t = 0;
+        if (t < n && t < rows_live && s_dep[t] < a.cap) cnt_t = max(0, s_cnt[t] - s_r[t]);
+        int M = 0;
+        const int off = block_exclusive_sum(cnt_t, s_itmp, &M);
+        if (M == 0) break;                                        // uniform
+        for (int j = 0; j < cnt_t; ++j) {
+            const int key = t * KT + s_r[t] + j;
+            c_sc[off + j] = s_nsc[t] + s_lp[key];
+            c_key[off + j] = key;
+        }
+        int P = 1;
+        while (P < M) P <<= 1;
+        for (int i = M + t; i < P; i += kBuildThreads) {
+            c_sc[i] = ninf;
+            c_key[i] = 0x7fffffff;
+        }
+        __syncthreads();
+        // bitonic sort into the loop's order: larger score first, then smaller key
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = t; i < P / 2; i += kBuildThreads) {
+                    const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+                    const double xs = c_sc[lo], ys = c_sc[hi];
+                    const int xk = c_key[lo], yk = c_key[hi];
+                    const bool y_first = ys > xs || (ys == xs && yk < xk);
+                    const bool down = (lo & size) == 0;               // this block sorts into the loop's order
+                    if (down ? y_first : !y_first) {
+                        c_sc[lo] = ys;
+                        c_sc[hi] = xs;
+                        c_key[lo] = yk;
+                        c_key[hi] = xk;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // the prefix the serial loop would take: candidate i becomes node n + i
+        const int m = min(M, nb - n);
+        double cand = ninf, child = ninf;
+        if (t < m) {
+            const int u = n + t, v = c_key[t] / KT;
+            cand = c_sc[t];
+            if (s_dep[v] + 1 < a.cap && u < rows_live && s_cnt[u] > 0) child = cand + s_lp[u * KT];
+        }
+        const double best_new = block_exclusive_max(child, s_dtmp);
+        if (t == 0) s_itmp[0] = m;
+        __syncthreads();
+        if (t < m && !(cand >= best_new)) atomicMin(&s_itmp[0], t);
+        __syncthreads();
+        const int k = s_itmp[0];
+        // grow them
+        if (t < k) {
+            const int u = n + t, key = c_key[t], v = key / KT;
+            par[u] = v;
+            tok[u] = s_tok[key];
+            if (sc) sc[u] = c_sc[t];
+            s_nsc[u] = c_sc[t];
+            s_dep[u] = s_dep[v] + 1;
+            atomicMax(&s_r[v], key - v * KT + 1);
+        }
+        __syncthreads();
+        n += k;
+        if (k < 4) break;                                         // uniform
+    }
+    return n;
+}
+
 // ---------------------------------------------------------------- the kernel
 
 template <typename T, int KT>
@@ -314,6 +468,13 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     __shared__ double s_s[kNW];
     __shared__ int s_last;
     __shared__ double s_exp2[256];                            // 2^(j/256) for exp_tab
+    // growth in batches: grown nodes' scores, depths, next child ranks; candidates
+    __shared__ double s_nsc[JF_MAX_NODES];
+    __shared__ int s_dep[JF_MAX_NODES], s_r[JF_MAX_NODES];
+    __shared__ double c_sc[JF_MAX_NODES * KT];
+    __shared__ int c_key[JF_MAX_NODES * KT];
+    __shared__ double s_dtmp[kBuildThreads];
+    __shared__ int s_itmp[kBuildThreads];
     static_assert(sizeof(K) * kBuildThreads * KT <= sizeof(double) * JF_MAX_NODES * KT, "key scratch");
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -539,7 +700,9 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
         s_cnt[t] = cnt;
     }
     __syncthreads();
-    if (w == 0) grow_tree<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt);
+    const int n0 = grow_batches<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt, s_nsc, s_dep, s_r, c_sc, c_key, s_dtmp,
+                                    s_itmp);
+    if (w == 0) grow_tree<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt, n0, s_nsc, s_dep, s_r);
 }
 
 // ---------------------------------------------------------------- host side
