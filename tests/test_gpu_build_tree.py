@@ -114,3 +114,27 @@ def test_build_tree_workspace_reused_across_shapes(jf):
     for _ in range(2):
         _compare(jf, big.logits, 4, 8, None, what="reuse: 4 x 64 x 40000")
         _compare(jf, small.logits, 2, 3, None, what="reuse: 1 x 9 x 300")
+
+
+def test_build_tree_exact_ties_across_batches(jf):
+    # one-hot rows (a single finite logit: that child's log-probability is exactly 0,
+    # so it scores what its parent scores) and two-way rows (two equal finite maxima:
+    # -ln 2 each) make candidates tie exactly with the children of nodes grown in the
+    # same batch; the grown tree must still follow the serial tie rule (the parent that
+    # joined first, then the child's rank). Sequence 2 is all one-hot: every score is 0.
+    case = W.make_draft_logits_case(41, 3, 48, 500, topk=3, max_path_nodes=10)
+    z = case.logits.clone()
+    rng = np.random.Generator(np.random.PCG64(41))
+    for b, rows in ((0, [0, 2, 5, 9, 11, 20]), (1, [1, 3, 4, 8]), (2, list(range(48)))):
+        for r in rows:
+            keep = rng.choice(500, size=1, replace=False)
+            row = torch.full((500,), float("-inf"), dtype=z.dtype)
+            row[keep] = z[b, r, keep]
+            z[b, r] = row
+    for b, r in ((0, 3), (0, 7), (1, 0), (1, 6)):
+        keep = rng.choice(500, size=2, replace=False)
+        row = torch.full((500,), float("-inf"), dtype=z.dtype)
+        row[keep] = 1.5
+        z[b, r] = row
+    _compare(jf, z, 3, 10, None, what="exact ties across batches")
+    _compare(jf, z, 3, 48, None, what="exact ties, no depth cap")
