@@ -125,6 +125,25 @@ typedef struct {
 size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_prefix_len);
 
 /*
+ * jf_tree_attention_plan -- the launch plan jf_tree_attention would use for a
+ * bf16 call of this shape (for tuning, tests and capacity planning; nothing is
+ * launched). plan: int32 [8], host memory, receives
+ *   [0] query rows per workgroup (packed GQA rows: node * G + head in group)
+ *   [1] key groups (waves that take alternate key tiles of one row block)
+ *   [2] 32-row blocks per wave
+ *   [3] splits per row block (prefix page ranges merged in the same launch;
+ *       includes the tree's own split when [6] is 1)
+ *   [4] prefix pages per split
+ *   [5] 1 when the batch schedule is planned on the device from the prefix
+ *       lengths (2 to 64 sequences), else 0
+ *   [6] 1 when the tree tiles run in a split of their own, else 0
+ *   [7] workgroups launched
+ * Host errors: those of jf_tree_attention's shape checks, JF_ERR_NULL (plan
+ * NULL), JF_ERR_UNSUPPORTED (fp32: one workgroup per 64 rows, no plan).
+ */
+jf_status jf_tree_attention_plan(const jf_attn_shape* s, int32_t max_prefix_len, int32_t* plan);
+
+/*
  * jf_tree_attention -- tree-causal attention over a paged prefix
  * (section 2 mask; section 3 paged verification).
  *

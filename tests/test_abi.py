@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
                "jf_commit_accepted", "jf_tree_attention_paged_tree", "jf_build_tree",
-               "jf_build_tree_workspace_bytes", "jf_tree_verify"):
+               "jf_build_tree_workspace_bytes", "jf_tree_verify", "jf_tree_attention_plan"):
         assert fn in names
 
 

@@ -1,0 +1,72 @@
+"""The attention launch plan (host logic, through jf_tree_attention_plan; no
+GPU): 32-row blocks with four key groups at budget 16, 64-row streaming blocks
+once many tiles fall to each workgroup, a grid that never exceeds one
+workgroup per CU unless the 1024-page split limit binds (room kept for the
+tree's own split), 7/8 of the CUs for one
+sequence in 256-row blocks, and the batch schedule for 2..64 sequences."""
+
+import itertools
+
+import pytest
+
+from test_abi import JF_ERR_NULL, JF_ERR_UNSUPPORTED, _shape
+
+
+@pytest.fixture(scope="module")
+def jf():
+    from tree_causal_attention_jf_amd import binding
+    return binding
+
+
+def plan(jf, max_prefix, **kw):
+    d = dict(B=1, N=16, Hq=32, Hkv=8, D=128, page_size=16)
+    d.update(kw)
+    pages = (max_prefix + 15) // 16 + 1
+    s = _shape(jf, num_pages=max(1, pages * d["B"]), max_pages_per_seq=max(1, pages), **d)
+    return jf.tree_attention_plan(s, max_prefix)
+
+
+def test_budget16_plan(jf):
+    p = plan(jf, 2048)
+    # 64 packed rows per KV head: two 32-row blocks, four key groups; 8 prefix splits + the tree's
+    assert (p["rows_per_workgroup"], p["key_groups"], p["splits"], p["tree_split"]) == (32, 4, 9, 1)
+    assert p["workgroups"] == 8 * 2 * 9 == 144
+
+
+def test_streaming_plan_for_long_prefixes(jf):
+    # batch 8 x 16384 at 16 nodes: one 64-row block (both row groups share every tile), two key groups
+    p = plan(jf, 16384, B=8)
+    assert (p["rows_per_workgroup"], p["key_groups"], p["balanced"]) == (64, 2, 1)
+    # one sequence switches at 32 tiles per workgroup, batches at 8
+    assert plan(jf, 16384)["rows_per_workgroup"] == 32
+    assert plan(jf, 32768)["rows_per_workgroup"] == 64
+    assert plan(jf, 2048, B=4)["rows_per_workgroup"] == 64
+    assert plan(jf, 2048, B=2)["rows_per_workgroup"] == 32
+
+
+def test_one_sequence_grid_never_exceeds_the_cus(jf):
+    for L, N, Hkv, G in itertools.product((16, 700, 2048, 4096, 8192, 32768, 100000), (1, 16, 64, 256),
+                                         (1, 4, 8), (1, 4, 8)):
+        p = plan(jf, L, N=N, Hkv=Hkv, Hq=Hkv * G)
+        # unless a split's page list (at most 1024 pages) forces more splits
+        assert p["workgroups"] <= 256 or p["pages_per_split"] == 1024, (L, N, Hkv, G, p)
+        assert p["splits"] >= 1 and p["pages_per_split"] % 4 == 0
+
+
+def test_one_sequence_256_row_blocks_leave_cus_free(jf):
+    p = plan(jf, 8192, N=256)
+    assert (p["rows_per_workgroup"], p["splits"], p["workgroups"]) == (256, 7, 224)
+
+
+def test_batches_use_the_device_schedule(jf):
+    assert plan(jf, 4096, B=8, N=256)["balanced"] == 1
+    assert plan(jf, 4096, B=65, N=16)["balanced"] == 0
+    assert plan(jf, 4096, B=1, N=256)["balanced"] == 0
+
+
+def test_plan_host_errors(jf):
+    import ctypes
+    s = _shape(jf)
+    assert jf._lib.jf_tree_attention_plan(ctypes.byref(s), 2048, None) == JF_ERR_NULL
+    out = (ctypes.c_int32 * 8)()
+    assert jf._lib.jf_tree_attention_plan(ctypes.byref(_shape(jf, dtype=jf.JF_F32)), 2048, out) == JF_ERR_UNSUPPORTED

@@ -39,6 +39,7 @@ EXPORTED = (
     "jf_build_tree_workspace_bytes",
     "jf_build_tree",
     "jf_tree_verify",
+    "jf_tree_attention_plan",
 )
 
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_build_ancestor_mask.argtypes = [vp, i32, i32, vp, vp, vp, vp]
     lib.jf_tree_attention_workspace_bytes.restype = sz
     lib.jf_tree_attention_workspace_bytes.argtypes = [ctypes.POINTER(AttnShape), i32]
+    lib.jf_tree_attention_plan.restype = i32
+    lib.jf_tree_attention_plan.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(ctypes.c_int32)]
     lib.jf_tree_attention.restype = i32
     lib.jf_tree_attention.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -197,6 +200,17 @@ def attn_shape(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor
 
 def tree_attention_workspace_bytes(shape: AttnShape, max_prefix_len: int) -> int:
     return int(_lib.jf_tree_attention_workspace_bytes(ctypes.byref(shape), int(max_prefix_len)))
+
+
+PLAN_FIELDS = ("rows_per_workgroup", "key_groups", "row_blocks_per_wave", "splits", "pages_per_split", "balanced",
+               "tree_split", "workgroups")
+
+
+def tree_attention_plan(shape: AttnShape, max_prefix_len: int) -> dict:
+    """The launch plan jf_tree_attention would use (bf16; nothing is launched)."""
+    out = (ctypes.c_int32 * 8)()
+    _check("jf_tree_attention_plan", _lib.jf_tree_attention_plan(ctypes.byref(shape), int(max_prefix_len), out))
+    return dict(zip(PLAN_FIELDS, list(out)))
 
 
 def tree_attention(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc,

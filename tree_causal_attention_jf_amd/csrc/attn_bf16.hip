@@ -1346,6 +1346,18 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                       : launch_verify_d<64>(p, a, c, accept_grid, stream);
 }
 
+void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int32_t* out) {
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    out[0] = p.rb;
+    out[1] = p.kw;
+    out[2] = p.rpw;
+    out[3] = p.splits;
+    out[4] = p.pps;
+    out[5] = p.balanced;
+    out[6] = p.tree_split;
+    out[7] = (int32_t)p.grid;
+}
+
 size_t attention_bf16_workspace_bytes(const jf_attn_shape& s, int max_prefix) {
     return plan_attention_bf16(s, max_prefix).bytes;
 }
