@@ -133,3 +133,15 @@ def test_paged_tree_bad_lengths_and_missing_pages_give_nan(jf):
     case.block_table = table
     out, lse = _run(jf, case, tree_len=tl)
     assert torch.isnan(out[:, :].float()).all() and torch.isnan(lse).all()
+
+
+def test_paged_tree_default_streaming_plan(jf):
+    # 16-node frames at 4 query heads per KV head (64 rows) over prefixes long enough that
+    # the default plan takes one 64-row block with two key groups; budgets ragged
+    from tree_causal_attention_jf_amd import binding
+    case = W.make_paged_tree_case(31, [2100, 1990, 2048, 1500], [16, 9, 1, 12], N=16, Hq=32, Hkv=8, D=128,
+                                  tree=("random", 6))
+    shape = binding.attn_shape(case.q, case.k_pages, case.block_table, case.sm_scale)
+    assert binding.tree_attention_plan(shape, case.max_prefix_len)["rows_per_workgroup"] == 64
+    out, lse = _run(jf, case)
+    _check(case, out, lse, what="default streaming plan")
