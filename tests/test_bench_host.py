@@ -50,3 +50,23 @@ def test_more_than_one_gpu_is_refused():
                        stderr=subprocess.PIPE, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("K,per", [(20, 40), (40, 40), (95, 40), (0, 40), (1, 1), (7, 3)])
+def test_graph_chunks_cover_exactly_k_steps_in_order(K, per):
+    plan = bench.plan_graph_chunks(K, per)
+    # consecutive, in order, exactly K steps
+    first = 0
+    for start, count in plan:
+        assert start == first and 1 <= count <= per
+        first += count
+    assert first == K
+    # whole passes start on set 0; at most one shorter replay, and it comes last
+    assert all(count == per and start % per == 0 for start, count in plan[:-1])
+    assert sum(1 for _, count in plan if count < per) == (1 if K % per else 0)
+
+
+def test_fewer_steps_than_input_sets_is_one_short_graph():
+    assert bench.plan_graph_chunks(20, 40) == [(0, 20)]
+    assert bench.plan_graph_chunks(40, 40) == [(0, 40)]
+    assert bench.plan_graph_chunks(95, 40) == [(0, 40), (40, 40), (80, 15)]
