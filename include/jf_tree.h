@@ -28,8 +28,10 @@
  *   - Ancestor bitset `anc`: uint64 [B, N, 4]; node j is bit (j % 64) of word
  *     (j / 64); row i has the bits of every node on the root-to-i path,
  *     i itself included. Bits >= N are zero.
- *   - Thread safety: the library keeps no mutable global state. Two calls in
- *     flight at the same time must not share a workspace.
+ *   - Thread safety: the library keeps no mutable global state besides the
+ *     per-device address of the fixed scratch array of jf_tree_verify_noalloc
+ *     (looked up once per device, under a lock). Two calls in flight at the
+ *     same time must not share a workspace.
  */
 #ifndef JF_TREE_H
 #define JF_TREE_H
@@ -51,7 +53,9 @@ enum {
     JF_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. D not 64/128)   */
     JF_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required         */
     JF_ERR_LAUNCH = 6,       /* the HIP runtime refused a launch                */
-    JF_ERR_ALIGN = 7         /* a pointer is not 16-byte aligned                */
+    JF_ERR_ALIGN = 7,        /* a pointer is not 16-byte aligned                */
+    JF_ERR_SCRATCH = 8       /* jf_tree_verify_noalloc: the call needs more than
+                                JF_NOALLOC_SCRATCH_BYTES of scratch             */
 };
 
 /* Element types of floating-point arrays. */
@@ -68,6 +72,9 @@ enum { JF_F32 = 0, JF_BF16 = 1 };
 /* Size of the counter region at the start of every workspace (see the
  * workspace notes of jf_tree_attention and jf_tree_accept). */
 #define JF_WORKSPACE_COUNTER_BYTES 4096
+/* Size of the fixed device array jf_tree_verify_noalloc takes its scratch
+ * from (32 MiB on every GPU the library is loaded on). */
+#define JF_NOALLOC_SCRATCH_BYTES 33554432
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* jf_status_string(jf_status s);
@@ -296,6 +303,37 @@ jf_status jf_tree_verify(const jf_attn_shape* s, int32_t max_prefix_len, const v
                          const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                          int32_t* accepted_nodes, int32_t* bonus_token, void* accept_workspace,
                          size_t accept_workspace_bytes, hipStream_t stream);
+
+/*
+ * jf_tree_verify_noalloc -- jf_tree_verify for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. It takes no workspace arguments; both
+ * workspaces are carved from a fixed device array of the library
+ * (JF_NOALLOC_SCRATCH_BYTES, 32 MiB per GPU, held from the library's load on
+ * that GPU until the process ends). The call itself allocates nothing and
+ * frees nothing.
+ *
+ * Arguments, results and host errors are those of jf_tree_verify without the
+ * two workspaces, plus JF_ERR_SCRATCH when the acceptance workspace (rounded
+ * up to 256 bytes) and the attention workspace together exceed
+ * JF_NOALLOC_SCRATCH_BYTES (e.g. batch 32 with 64-node trees at 32q/4kv); the
+ * sizes come from jf_tree_accept_workspace_bytes and
+ * jf_tree_attention_workspace_bytes. Every call first clears the counter
+ * regions of both workspaces with a small kernel on `stream`, so the
+ * contents left by an earlier call never matter; JF_ERR_LAUNCH when the
+ * array's address on the stream's device cannot be looked up.
+ *
+ * All calls on one GPU share that GPU's array: two calls in flight at the
+ * same time on one GPU (on different streams, or from different threads)
+ * race and give undefined results. Calls on one stream never overlap.
+ */
+jf_status jf_tree_verify_noalloc(const jf_attn_shape* s, int32_t max_prefix_len, const void* q,
+                                 const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                 const int32_t* prefix_len, const void* k_tree, const void* v_tree, uint64_t* anc,
+                                 int32_t anc_from_parent, void* out, float* lse, int32_t vocab,
+                                 const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
+                                 const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                                 int32_t* accepted_nodes, int32_t* bonus_token, hipStream_t stream);
 
 /*
  * jf_commit_accepted -- append each sequence's accepted path to its paged KV

@@ -14,7 +14,8 @@ from conftest import ROOT
 HEADER = os.path.join(ROOT, "include", "jf_tree.h")
 LIB = os.path.join(ROOT, "tree_causal_attention_jf_amd", "libjf_tree.so")
 
-JF_OK, JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_DTYPE, JF_ERR_UNSUPPORTED, JF_ERR_WORKSPACE, JF_ERR_LAUNCH, JF_ERR_ALIGN = range(8)
+(JF_OK, JF_ERR_NULL, JF_ERR_SHAPE, JF_ERR_DTYPE, JF_ERR_UNSUPPORTED, JF_ERR_WORKSPACE, JF_ERR_LAUNCH, JF_ERR_ALIGN,
+ JF_ERR_SCRATCH) = range(9)
 
 
 def _declared():
@@ -36,7 +37,8 @@ def test_header_declares_the_boundary():
     for fn in ("jf_build_ancestor_mask", "jf_tree_attention", "jf_tree_accept", "jf_status_string",
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
                "jf_commit_accepted", "jf_tree_attention_paged_tree", "jf_build_tree",
-               "jf_build_tree_workspace_bytes", "jf_tree_verify", "jf_tree_attention_plan"):
+               "jf_build_tree_workspace_bytes", "jf_tree_verify", "jf_tree_attention_plan",
+               "jf_tree_verify_noalloc"):
         assert fn in names
 
 
@@ -53,13 +55,15 @@ def test_header_limits_match_the_binding(binding):
     text = open(HEADER).read()
     for name, value in (("JF_MAX_NODES", binding.MAX_NODES), ("JF_PAGE_SIZE", binding.PAGE_SIZE),
                         ("JF_MAX_BATCH", binding.JF_MAX_BATCH), ("JF_MAX_TOPK", binding.JF_MAX_TOPK),
-                        ("JF_WORKSPACE_COUNTER_BYTES", binding.JF_WORKSPACE_COUNTER_BYTES)):
+                        ("JF_WORKSPACE_COUNTER_BYTES", binding.JF_WORKSPACE_COUNTER_BYTES),
+                        ("JF_NOALLOC_SCRATCH_BYTES", binding.JF_NOALLOC_SCRATCH_BYTES)):
         assert re.search(r"#define %s (\d+)" % name, text).group(1) == str(value), name
 
 
 def test_status_strings_and_version(binding):
-    for code in range(8):
+    for code in range(9):
         assert binding.status_string(code)
+    assert "JF_NOALLOC_SCRATCH_BYTES" in binding.status_string(JF_ERR_SCRATCH)
     assert binding.status_string(99) == "unknown status"
     assert re.match(r"^\d+\.\d+\.\d+$", binding.version())
 
@@ -297,3 +301,38 @@ def test_verify_host_checks(binding):
     assert ver(from_parent=1, nul=("anc",)) == JF_ERR_NULL          # the built bitsets need somewhere to go
     assert ver(shape=_shape(binding, B=0)) == JF_OK                 # empty batch: no launch
     assert ver(shape=_shape(binding, B=0), from_parent=1) == JF_OK
+
+
+def test_noalloc_verify_host_checks(binding):
+    """jf_tree_verify_noalloc applies jf_tree_verify's checks and refuses a call
+    whose two workspaces would not fit its fixed array, all before any HIP call
+    (nothing here touches a device)."""
+    L = binding._lib
+    p = ctypes.c_void_p(16)
+
+    def ver(shape, max_prefix=2048, logits=p, dt=1, V=1000, nul=(), from_parent=0):
+        a = {n: p for n in ("q", "kp", "vp", "bt", "pl", "kt", "vt", "anc", "out", "draft", "parent", "next",
+                            "alen", "nodes", "bonus")}
+        for n in nul:
+            a[n] = None
+        return L.jf_tree_verify_noalloc(ctypes.byref(shape), max_prefix, a["q"], a["kp"], a["vp"], a["bt"],
+                                        a["pl"], a["kt"], a["vt"], a["anc"], from_parent, a["out"], None, V, logits,
+                                        dt, a["draft"], a["parent"], a["next"], a["alen"], a["nodes"], a["bonus"],
+                                        None)
+
+    shape = _shape(binding)
+    assert ver(_shape(binding, N=0)) == JF_ERR_SHAPE
+    assert ver(_shape(binding, D=96)) == JF_ERR_UNSUPPORTED
+    assert ver(shape, logits=None) == JF_ERR_NULL
+    assert ver(shape, dt=5) == JF_ERR_DTYPE
+    assert ver(shape, V=0) == JF_ERR_SHAPE
+    for n in ("q", "anc", "out", "draft", "parent", "next", "alen", "nodes", "bonus"):
+        assert ver(shape, nul=(n,)) == JF_ERR_NULL, n
+    assert ver(shape, from_parent=2) == JF_ERR_SHAPE
+    assert ver(shape, nul=("q",)) == JF_ERR_NULL
+    # batch 32 of 64-node trees at 32q/4kv over prefixes up to 8192 needs more than the array
+    big = _shape(binding, B=32, N=64, Hq=32, Hkv=4, num_pages=20000, max_pages_per_seq=512)
+    need = binding.tree_attention_workspace_bytes(big, 8192) + binding.tree_accept_workspace_bytes(32, 64, 151936)
+    assert need > binding.JF_NOALLOC_SCRATCH_BYTES
+    assert ver(big, max_prefix=8192, V=151936) == JF_ERR_SCRATCH
+    assert ver(_shape(binding, B=0)) == JF_OK                       # empty batch: nothing looked up or launched

@@ -25,6 +25,8 @@ PAGE_SIZE = 16
 JF_MAX_BATCH = 1024          # sequences per tree_attention call (include/jf_tree.h)
 JF_MAX_TOPK = 8              # children per node in build_tree
 JF_WORKSPACE_COUNTER_BYTES = 4096   # counter region at the start of every workspace
+JF_NOALLOC_SCRATCH_BYTES = 33554432  # fixed scratch array of jf_tree_verify_noalloc (per GPU)
+JF_ERR_SCRATCH = 8
 
 EXPORTED = (
     "jf_status_string",
@@ -40,6 +42,7 @@ EXPORTED = (
     "jf_build_tree",
     "jf_tree_verify",
     "jf_tree_attention_plan",
+    "jf_tree_verify_noalloc",
 )
 
 
@@ -91,6 +94,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_verify.restype = i32
     lib.jf_tree_verify.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                    vp, sz, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jf_tree_verify_noalloc.restype = i32
+    lib.jf_tree_verify_noalloc.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                           vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.jf_tree_attention_paged_tree.restype = i32
     lib.jf_tree_attention_paged_tree.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  vp, vp, sz, vp]
@@ -373,6 +379,41 @@ def tree_verify(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, an
                              _ptr(next_tokens), _ptr(accept_len), _ptr(accepted_nodes), _ptr(bonus_token),
                              _ptr(cws), cws_bytes, _stream(dev))
     _check("jf_tree_verify", st)
+    return out, lse, accept_len, accepted_nodes, bonus_token, next_tokens, anc
+
+
+def tree_verify_noalloc(q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc, parent, draft, logits,
+                        out, next_tokens, accept_len, accepted_nodes, bonus_token, sm_scale: Optional[float] = None,
+                        max_prefix_len: int = 0, lse: Optional[torch.Tensor] = None,
+                        anc_out: Optional[torch.Tensor] = None):
+    """tree_verify for callers that cannot allocate: the library takes its scratch
+    from a fixed device array (JF_NOALLOC_SCRATCH_BYTES per GPU), and this wrapper
+    allocates nothing either, so every output buffer is the caller's and
+    max_prefix_len must be given. anc None: the bitsets are built from parent into
+    anc_out. Calls that overlap on one GPU race (see include/jf_tree.h)."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (k_tree, "k_tree"), (v_tree, "v_tree"),
+                 (out, "out")):
+        _need(t, n, q.dtype)
+    for t, n in ((block_table, "block_table"), (prefix_len, "prefix_len"), (parent, "parent"), (draft, "draft"),
+                 (next_tokens, "next_tokens"), (accept_len, "accept_len"), (accepted_nodes, "accepted_nodes"),
+                 (bonus_token, "bonus_token")):
+        _need(t, n, torch.int32)
+    _need(logits, "logits")
+    from_parent = anc is None
+    if from_parent:
+        if anc_out is None:
+            raise ValueError("anc None builds the bitsets into anc_out, which must be given")
+        anc = anc_out
+    _need(anc, "anc", torch.uint64)
+    ldt = {torch.bfloat16: JF_BF16, torch.float32: JF_F32}[logits.dtype]
+    shape = attn_shape(q, k_pages, block_table, sm_scale)
+    dev = q.device
+    st = _lib.jf_tree_verify_noalloc(ctypes.byref(shape), int(max_prefix_len), _ptr(q), _ptr(k_pages),
+                                     _ptr(v_pages), _ptr(block_table), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree),
+                                     _ptr(anc), 1 if from_parent else 0, _ptr(out), _ptr(lse), logits.shape[-1],
+                                     _ptr(logits), ldt, _ptr(draft), _ptr(parent), _ptr(next_tokens),
+                                     _ptr(accept_len), _ptr(accepted_nodes), _ptr(bonus_token), _stream(dev))
+    _check("jf_tree_verify_noalloc", st)
     return out, lse, accept_len, accepted_nodes, bonus_token, next_tokens, anc
 
 

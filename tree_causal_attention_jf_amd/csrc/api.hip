@@ -3,6 +3,8 @@
 // touches neither the device nor the caller's buffers.
 #include <math.h>
 
+#include <mutex>
+
 #include "jf_common.h"
 
 namespace jf {
@@ -79,6 +81,9 @@ const char* jf_status_string(jf_status s) {
         case JF_ERR_WORKSPACE: return "workspace missing or too small";
         case JF_ERR_LAUNCH: return "kernel launch failed";
         case JF_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case JF_ERR_SCRATCH:
+            return "the call needs more scratch than the fixed array of jf_tree_verify_noalloc holds "
+                   "(JF_NOALLOC_SCRATCH_BYTES); use jf_tree_verify with caller workspaces";
         default: return "unknown status";
     }
 }
@@ -308,6 +313,103 @@ jf_status jf_build_tree(int32_t B, int32_t N, int32_t vocab, const void* draft_l
     const hipError_t e = jf::launch_build(B, N, vocab, draft_logits, logits_dtype, topk, max_path_nodes, budget,
                                           parent, token, score, tree_len, workspace, stream);
     return e == hipSuccess ? JF_OK : JF_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- verification without allocation
+
+namespace {
+
+// The fixed scratch of jf_tree_verify_noalloc: its acceptance workspace, then its
+// attention workspace, each starting with its own counter region. Every GPU the
+// library is loaded on holds one copy (zero-initialised with the code object)
+// until the process ends.
+static __device__ __align__(256) char scratch[JF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Zero the counter regions of both workspaces (a kernel, not a memset, so the
+// call can be captured into a graph).
+__global__ void clear_counter_regions(int* accept_counters, int* attn_counters) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < jf::kMaxCounters) {
+        accept_counters[i] = 0;
+        if (attn_counters) attn_counters[i] = 0;
+    }
+}
+
+// Device address of `scratch` on device `dev` (looked up once per device, with
+// that device current). The array's name is a host-side stand-in, never passed
+// to a kernel.
+hipError_t scratch_on_device(int dev, char** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+jf_status jf_tree_verify_noalloc(const jf_attn_shape* s, int32_t max_prefix_len, const void* q,
+                                 const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                 const int32_t* prefix_len, const void* k_tree, const void* v_tree, uint64_t* anc,
+                                 int32_t anc_from_parent, void* out, float* lse, int32_t vocab,
+                                 const void* target_logits, int32_t logits_dtype, const int32_t* draft_tokens,
+                                 const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
+                                 int32_t* accepted_nodes, int32_t* bonus_token, hipStream_t stream) {
+    // the host checks of jf_tree_verify, with workspaces of the required sizes
+    // standing in for the fixed array (nothing is launched or looked up before
+    // the call is known to be valid)
+    jf_status st = check_attention_call(s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree,
+                                        v_tree, anc, out, reinterpret_cast<void*>(256), ~(size_t)0);
+    if (st != JF_OK) return st;
+    if (!target_logits) return JF_ERR_NULL;
+    if (anc_from_parent != 0 && anc_from_parent != 1) return JF_ERR_SHAPE;
+    st = check_accept_call(s->B, s->N, vocab, target_logits, logits_dtype, nullptr, draft_tokens, parent, anc,
+                           next_tokens, accept_len, accepted_nodes, bonus_token, reinterpret_cast<void*>(256),
+                           ~(size_t)0);
+    if (st != JF_OK) return st;
+    const size_t acc_need = jf::accept_workspace_bytes(s->B, s->N, vocab);
+    const size_t attn_need = jf_tree_attention_workspace_bytes(s, max_prefix_len);
+    const size_t attn_off = align256(acc_need);
+    if (attn_off + attn_need > (size_t)JF_NOALLOC_SCRATCH_BYTES) return JF_ERR_SCRATCH;
+    if (s->B == 0) return JF_OK;
+
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return JF_ERR_LAUNCH;
+    char* base = nullptr;
+    if (scratch_on_device(dev, &base) != hipSuccess) return JF_ERR_LAUNCH;
+    char* acc_ws = base;
+    char* attn_ws = attn_need > 0 ? base + attn_off : nullptr;
+    hipLaunchKernelGGL(clear_counter_regions, dim3((jf::kMaxCounters + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<int*>(acc_ws), reinterpret_cast<int*>(attn_ws));
+    if (hipGetLastError() != hipSuccess) return JF_ERR_LAUNCH;
+    return jf_tree_verify(s, max_prefix_len, q, k_pages, v_pages, block_table, prefix_len, k_tree, v_tree, anc,
+                          anc_from_parent, out, lse, attn_ws, attn_need, vocab, target_logits, logits_dtype,
+                          draft_tokens, parent, next_tokens, accept_len, accepted_nodes, bonus_token, acc_ws,
+                          acc_need, stream);
 }
 
 }  // extern "C"
