@@ -336,3 +336,18 @@ def test_noalloc_verify_host_checks(binding):
     assert need > binding.JF_NOALLOC_SCRATCH_BYTES
     assert ver(big, max_prefix=8192, V=151936) == JF_ERR_SCRATCH
     assert ver(_shape(binding, B=0)) == JF_OK                       # empty batch: nothing looked up or launched
+
+
+def test_workspace_cache_keeps_replaced_buffers_alive(binding):
+    """A workspace replaced by a larger one stays referenced, so a graph that
+    captured the old address never writes into memory another tensor owns."""
+    import torch
+    ws = binding.Workspace()
+    dev = torch.device("cpu")
+    a = ws.get(dev, "attn", 1000)
+    assert ws.get(dev, "attn", 500) is a                # big enough: reused
+    assert int(a.sum()) == 0
+    b = ws.get(dev, "attn", 5000)                       # grown: a new zeroed buffer
+    assert b is not a and b.numel() >= 5000 and int(b.sum()) == 0
+    assert any(r is a for r in ws.retired())
+    assert ws.get(dev, "accept", 0) is None

@@ -151,10 +151,16 @@ class Workspace:
     library leaves the fixed counter region at the start of a workspace zero
     after every call and writes the rest before reading it, so a buffer is
     cleared only when it is first allocated or grown, and serves calls of any
-    shape. Not for calls that are in flight concurrently on different streams."""
+    shape. Not for calls that are in flight concurrently on different streams.
+
+    A buffer replaced by a larger one is kept alive (never returned to the
+    caching allocator) for as long as this object lives: a graph captured with
+    the old buffer still writes its counters and partials there on replay, and
+    no other tensor may own that memory meanwhile."""
 
     def __init__(self):
         self._bufs = {}
+        self._retired = []
         self._lock = threading.Lock()
 
     def get(self, device: torch.device, key: str, nbytes: int) -> Optional[torch.Tensor]:
@@ -164,9 +170,16 @@ class Workspace:
             k = (str(device), key)
             buf = self._bufs.get(k)
             if buf is None or buf.numel() < nbytes:
+                if buf is not None:
+                    self._retired.append(buf)
                 buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
                 self._bufs[k] = buf
             return buf
+
+    def retired(self):
+        """Buffers replaced by larger ones and still held (see the class note)."""
+        with self._lock:
+            return list(self._retired)
 
 
 _default_ws = Workspace()

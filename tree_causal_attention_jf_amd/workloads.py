@@ -3,9 +3,19 @@
 This module draws random numbers and lays them out: draft trees (as parent
 arrays), a paged KV cache with shuffled page order, queries, the tree's own
 K/V, target logits or target ids, and draft tokens. It computes nothing that
-the attention or acceptance path computes: no ancestor sets, no scores, no
-softmax, no argmax. Both the CPU oracle's tests and the GPU path's tests and
-benchmark take their inputs from here, as plain CPU tensors.
+the attention or acceptance path computes: no ancestor sets, no attention
+scores or weights, no argmax over target logits. Both the CPU oracle's tests
+and the GPU path's tests and benchmark take their inputs from here, as plain
+CPU tensors.
+
+One exception shapes inputs only: `tree_best_first` grows the best-first
+draft trees of the budget-64/256 workloads the way the workload text
+describes them, so it normalises its own random draft logits (a log-softmax)
+and takes their top-k, i.e. it repeats the arithmetic of tree construction.
+Its trees are inputs to attention and acceptance; no expected value comes
+from it. Tree construction itself (jf_build_tree) is checked against the
+oracle's build_tree on separately drawn logits (make_draft_logits_case), never
+against this function.
 
 The workloads stand in for the evaluation set-up of "JetFlow: Breaking the
 Scaling Ceiling of Speculative Decoding with Parallel Tree Drafting"
