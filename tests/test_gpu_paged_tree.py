@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from tree_causal_attention_jf_amd import workloads as W
+from plan_items import assert_items_covered, item_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -120,9 +121,11 @@ def test_paged_tree_budget256_sampled(jf):
     budgets = rng.integers(16, 257, size=8).tolist()
     case = W.make_paged_tree_case(31, lens, budgets, N=256, Hq=32, Hkv=8, D=128, tree=("best_first", 4, 12, 2.0))
     out, lse = _run(jf, case)
-    rows = sorted({(b, int(rng.integers(budgets[b])), int(rng.integers(32))) for b in range(8) for _ in range(6)}
-                  | {(b, budgets[b] - 1, 31) for b in range(8)})
-    _check(case, out, lse, rows=rows, what=f"budgets {budgets}")
+    # every live (sequence, KV head, row block) item of the plan has a node with all heads compared
+    rows, items, plan = item_rows(jf, case, 5, tree_len=budgets)
+    assert_items_covered(case, rows, items, plan)
+    rows = sorted(set(rows) | {(b, budgets[b] - 1, 31) for b in range(8)})
+    _check(case, out, lse, rows=rows, what=f"budgets {budgets}, {len(items)} plan items")
 
 
 def test_paged_tree_bad_lengths_and_missing_pages_give_nan(jf):

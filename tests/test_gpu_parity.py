@@ -22,6 +22,7 @@ import torch
 
 import oracle
 from tree_causal_attention_jf_amd import workloads as W
+from plan_items import assert_items_covered, item_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -342,8 +343,11 @@ def _sampled_rows(wl, count, seed):
 def test_attention_bf16_large_sampled(jf, name):
     for unscaled in (False, True):
         wl = W.make_workload(name, 0, with_accept=False, unscaled=unscaled)
-        out, lse = run_attention(jf, wl, to_dev(wl))
-        rows = _sampled_rows(wl, 48, 1)
+        d = to_dev(wl)
+        out, lse = run_attention(jf, wl, d)
+        rows, items, plan = item_rows(jf, wl, 1 + unscaled)
+        assert_items_covered(wl, rows, items, plan)
+        say(f"  {name}: plan {plan}, {len(items)} items, {len(rows)} rows compared")
         ref, lref = _oracle_full(wl, rows=rows)
         o = out.float().cpu().numpy()
         idx = tuple(np.array(rows).T)
@@ -365,8 +369,13 @@ def test_attention_bf16_streaming_plan(jf, B, lens, full):
     for unscaled in ((False, True) if full else (False,)):
         if unscaled:
             wl = W.make_workload("c1_chain16", 6, with_accept=False, B=B, prefix=("list", lens), unscaled=True)
-        out, lse = run_attention(jf, wl, to_dev(wl))
-        rows = None if full else _sampled_rows(wl, 48, 2)
+        d = to_dev(wl)
+        out, lse = run_attention(jf, wl, d)
+        rows = None
+        if not full:
+            rows, items, plan = item_rows(jf, wl, 2)
+            assert_items_covered(wl, rows, items, plan)
+            say(f"  streaming B {B}: plan {plan}, {len(items)} items, {len(rows)} rows compared")
         ref, lref = _oracle_full(wl, rows=rows)
         if full:
             check_bf16(out, ref, lse, lref, f"streaming B {B}{' unscaled' if unscaled else ''}",
