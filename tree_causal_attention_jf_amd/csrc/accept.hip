@@ -27,9 +27,11 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_ids_kernel(
 }
 
 
-template <typename T>
+// PATHS 1: every chunk fits in registers; 2: chunks are scanned in batches
+// (one instantiation each, so neither carries the other's registers)
+template <typename T, int PATHS>
 __global__ __launch_bounds__(kAcceptThreads) void accept_logits_kernel(AcceptArgs a) {
-    accept_logits_body<T>(a, blockIdx.x);
+    accept_logits_body<T, PATHS>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- host side
@@ -114,10 +116,15 @@ hipError_t launch_accept(int B, int N, int vocab, const void* logits, int dtype,
     const AcceptArgs a = make_accept_args(p, N, vocab, logits, dtype, draft, parent, anc, next_tokens, accept_len,
                                           accepted_nodes, bonus, workspace);
     const dim3 grid((unsigned)((long)B * N * p.chunks));
-    if (dtype == JF_BF16)
-        hipLaunchKernelGGL(accept_logits_kernel<uint16_t>, grid, dim3(kAcceptThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(accept_logits_kernel<float>, grid, dim3(kAcceptThreads), 0, stream, a);
+    const int epv = dtype == JF_BF16 ? 8 : 4;
+    const bool in_regs = (p.chunk_len + epv - 1) / epv <= kRegChunkVecs;
+    if (dtype == JF_BF16) {
+        if (in_regs) hipLaunchKernelGGL((accept_logits_kernel<uint16_t, 1>), grid, dim3(kAcceptThreads), 0, stream, a);
+        else hipLaunchKernelGGL((accept_logits_kernel<uint16_t, 2>), grid, dim3(kAcceptThreads), 0, stream, a);
+    } else {
+        if (in_regs) hipLaunchKernelGGL((accept_logits_kernel<float, 1>), grid, dim3(kAcceptThreads), 0, stream, a);
+        else hipLaunchKernelGGL((accept_logits_kernel<float, 2>), grid, dim3(kAcceptThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

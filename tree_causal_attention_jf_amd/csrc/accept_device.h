@@ -69,7 +69,7 @@ static __device__ Best block_best(Best b, Best* scratch) {
 //   mism bit u: u > 0 and draft[u] != nxt[parent[u]]
 //   node v agrees along its path iff (anc[v] & mism) == 0
 //   end node = the agreeing node with most path nodes, smallest index on ties
-static __device__ void walk_sequence(int b, int N, int p_u, int d_u, const uint64_t a_u[kAncWords],
+static __device__ __forceinline__ void walk_sequence(int b, int N, int p_u, int d_u, const uint64_t a_u[kAncWords],
                               const int32_t* nxt, int32_t* __restrict__ accept_len,
                               int32_t* __restrict__ accepted_nodes, int32_t* __restrict__ bonus) {
     __shared__ uint64_t mism[kAncWords];
@@ -144,123 +144,238 @@ struct NodeIn {
     uint64_t a[kAncWords];
 };
 
+// Thread u's node. The loads are unconditional (threads u >= N read node N - 1,
+// whose values they never use: every consumer looks only at u < N), so the
+// compiler counts them exactly and a later wait for them does not also wait for
+// the loads issued after them.
 __device__ __forceinline__ NodeIn load_node(int b, int N, const int32_t* __restrict__ parent,
                                             const int32_t* __restrict__ draft, const uint64_t* __restrict__ anc) {
-    NodeIn n{-1, 0, {0, 0, 0, 0}};
-    const int u = threadIdx.x;
-    if (u < N) {
-        const size_t r = (size_t)b * N + u;
-        n.p = parent[r];
-        n.d = draft[r];
-        if (anc) {
-            #pragma unroll
-            for (int k = 0; k < kAncWords; ++k) n.a[k] = anc[r * kAncWords + k];
-        }
-    }
+    NodeIn n;
+    const size_t r = (size_t)b * N + min((int)threadIdx.x, N - 1);
+    n.p = parent[r];
+    n.d = draft[r];
+    #pragma unroll
+    for (int k = 0; k < kAncWords; ++k) n.a[k] = anc ? anc[r * kAncWords + k] : 0ull;
     return n;
 }
 
 
+// Chunks of at most this many 16-byte vectors are scanned from registers.
+constexpr int kRegChunkVecs = 16 * kAcceptThreads;
+
+// bf16 pair in one dword -> the two values as fp32 (low half first)
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Largest of the EPV values in a 16-byte vector, folded into m with v_max3
+// (a quiet NaN is ignored; a signalling NaN makes the result NaN).
 template <typename T>
-__device__ __forceinline__ void scan_chunk(const T* __restrict__ row, int lo, int hi, Best& b);
+__device__ __forceinline__ float vec_max(const u32x4 r, float m) {
+    if constexpr (sizeof(T) == 2) {
+        const float a = max3f(bf_hi(r[0]), bf_hi(r[1]), bf_hi(r[2]));
+        const float c = max3f(bf_hi(r[3]), bf_lo(r[0]), bf_lo(r[1]));
+        return max3f(max3f(bf_lo(r[2]), bf_lo(r[3]), a), c, m);
+    } else {
+        return max3f(max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2])),
+                     __uint_as_float(r[3]), m);
+    }
+}
 
-// bf16: 8 values per 16-byte load; the row start must be 16-byte aligned.
-// A thread visits its indices in increasing order, so a strictly larger value is
-// the only thing that can replace its best (an equal one comes later and loses).
-// Per 8 values: the max of the vector (v_max3 ignores NaN), and only when it beats
-// the best so far, the first position holding it. A thread that has recorded
-// nothing yet also takes a vector whose max equals its -inf start, so a row of
-// -inf values still yields its first index.
-__device__ __forceinline__ void offer8_bf16(const u32x4 r, int i0, Best& b) {
-    float v[8];
+// Value e (0 .. EPV-1, in index order) of a 16-byte vector.
+template <typename T>
+__device__ __forceinline__ float vec_val(const u32x4 r, int e) {
+    if constexpr (sizeof(T) == 2) return (e & 1) ? bf_hi(r[e >> 1]) : bf_lo(r[e >> 1]);
+    else return __uint_as_float(r[e]);
+}
+
+// Position (0 .. EPV-1) of the first value equal to m in a vector, or EPV.
+template <typename T>
+__device__ __forceinline__ int vec_first(const u32x4 r, float m) {
+    constexpr int EPV = 16 / (int)sizeof(T);
+    int k = EPV;
     #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(r[e] << 16);
-        v[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-    }
-    const float m = max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), max3f(v[6], v[7], v[7]));
-    if (m != m) {
-        // all NaN, or a signalling NaN among them: value by value
-        #pragma unroll
-        for (int e = 0; e < 8; ++e) offer(b, v[e], i0 + e);
-    } else if (m > b.v || (b.i == kNoIndex)) {
-        int k = 7;
-        #pragma unroll
-        for (int e = 6; e >= 0; --e) k = (v[e] == m) ? e : k;
-        b.v = m;
-        b.i = i0 + k;
-    }
+    for (int e = EPV - 1; e >= 0; --e) k = (vec_val<T>(r, e) == m) ? e : k;
+    return k;
 }
 
-template <>
-__device__ __forceinline__ void scan_chunk<uint16_t>(const uint16_t* __restrict__ row, int lo, int hi, Best& b) {
-    const int nvec = (hi - lo) >> 3;
+// Exact, value by value (a vector that holds a signalling NaN).
+template <typename T>
+__device__ __forceinline__ void vec_offer(const u32x4 r, int i0, Best& b) {
+    constexpr int EPV = 16 / (int)sizeof(T);
+    #pragma unroll
+    for (int e = 0; e < EPV; ++e) offer(b, vec_val<T>(r, e), i0 + e);
+}
+
+// Wave-wide max / min without LDS: DPP steps inside each row of 16 lanes (quad
+// permutations, then the half-row and row mirrors), then the four row results
+// read with readlane. The result is the same in every lane (scalar).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad1032>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad2301>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(v))));
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, (int)dpp_u32<kDppQuad1032>((uint32_t)v));
+    v = min(v, (int)dpp_u32<kDppQuad2301>((uint32_t)v));
+    v = min(v, (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v));
+    v = min(v, (int)dpp_u32<kDppRowMirror>((uint32_t)v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// The winner (largest value, smallest index; NaN never wins) of logits
+// row[lo, hi), over the workgroup. Every thread returns it. 16-byte
+// non-temporal loads, thread t taking vectors t, t + 256, t + 512, ...: the
+// row must start on a 16-byte boundary and hi - lo must be a multiple of the
+// values per vector (the acceptance plan keeps both for aligned rows). With set_n > 0, wave 0 builds the
+// ancestor sets of a tree of set_n <= 64 nodes from the parent entry set_p of
+// its lane (tree_set_wave) while the first loads are in flight, into set_out.
+//  * Up to KR vectors per thread (the acceptance plan's chunks when rows are
+//    few): every load is issued at once and the chunk stays in registers; each
+//    thread takes the max of its values with v_max3 (branch-free), the
+//    workgroup reduces it, and only a thread holding that max searches its
+//    vectors for the first position. A signalling NaN anywhere (the only way a
+//    v_max3 result is NaN) sends the chunk through the exact per-value path.
+//  * Longer chunks: batches of KB vectors, two in flight; a vector is searched
+//    only when its max beats the thread's best so far (indices rise within a
+//    thread, so a strictly larger value is the only replacement), value by
+//    value when it holds a signalling NaN.
+// PATHS: 0 either path, chosen from the chunk length; 1 the in-register path
+// only (the caller guarantees nvec <= KR * 256); 2 the batched path only.
+template <typename T, int PATHS = 0>
+__device__ __forceinline__ Best chunk_best(const T* __restrict__ row, int lo, int hi, Best* scratch, int set_p,
+                                           int set_n, uint64_t& set_out) {
+    __shared__ float s_max[kAcceptThreads / kWave];
+    __shared__ int s_idx[kAcceptThreads / kWave];
+    constexpr int EPV = 16 / (int)sizeof(T);
+    constexpr int KR = kRegChunkVecs / kAcceptThreads;
+    constexpr int KB = 4;
+    constexpr int TH = kAcceptThreads;
+    const float NEG = -__builtin_inff();
+    const int nvec = (hi - lo) / EPV;
     const u32x4* vp = reinterpret_cast<const u32x4*>(row + lo);
-    constexpr int U = 4;
-    constexpr int STEP = U * kAcceptThreads;
-    int k = threadIdx.x;
-    // two batches in flight: the next batch is requested before the current one is scanned
-    u32x4 cur[U];
-    const bool any = k + (U - 1) * kAcceptThreads < nvec;
-    if (any) {
+    const int t = threadIdx.x;
+    const int mine = nvec > t ? (nvec - 1 - t) / TH + 1 : 0;     // vectors t, t + TH, ... of this thread
+    // every load is unconditional (past the thread's last vector it re-reads the
+    // chunk's last one, which is never looked at), so the compiler counts them
+    // exactly and no wait covers more than it must
+    const int vlast = nvec - 1;                                  // nvec >= 1 for a non-empty chunk
+    if (PATHS == 1 || (PATHS == 0 && nvec <= KR * TH)) {
+        u32x4 v[KR];
         #pragma unroll
-        for (int j = 0; j < U; ++j) cur[j] = __builtin_nontemporal_load(vp + k + j * kAcceptThreads);
-    }
-    for (; k + (U - 1) * kAcceptThreads < nvec; k += STEP) {
-        u32x4 nxt[U];
-        const bool more = k + STEP + (U - 1) * kAcceptThreads < nvec;
-        if (more) {
-            #pragma unroll
-            for (int j = 0; j < U; ++j) nxt[j] = __builtin_nontemporal_load(vp + k + STEP + j * kAcceptThreads);
+        for (int j = 0; j < KR; ++j) v[j] = __builtin_nontemporal_load(vp + min(t + j * TH, vlast));
+        if (set_n > 0 && t < kWave) set_out = tree_set_wave(set_p, set_n);
+        float m = NEG;
+        #pragma unroll
+        for (int j = 0; j < KR; ++j) {
+            const float mj = vec_max<T>(v[j], m);
+            m = j < mine ? mj : m;
         }
-        #pragma unroll
-        for (int j = 0; j < U; ++j) offer8_bf16(cur[j], lo + ((k + j * kAcceptThreads) << 3), b);
-        if (more) {
-            #pragma unroll
-            for (int j = 0; j < U; ++j) cur[j] = nxt[j];
+        // the workgroup's max (and whether a signalling NaN showed up) in one exchange
+        const bool nan_t = m != m;
+        const float wm = wave_max_f32(nan_t ? NEG : m);
+        const bool wnan = __ballot(nan_t) != 0ull;
+        if ((t & 63) == 0) {
+            s_max[t >> 6] = wm;
+            s_idx[t >> 6] = wnan ? 1 : 0;
         }
-    }
-    for (; k < nvec; k += kAcceptThreads) offer8_bf16(__builtin_nontemporal_load(vp + k), lo + (k << 3), b);
-    for (int i = lo + (nvec << 3) + threadIdx.x; i < hi; i += kAcceptThreads)
-        offer(b, bf16_bits_to_f32(row[i]), i);
-}
-
-// fp32: 4 values per 16-byte load
-template <>
-__device__ __forceinline__ void scan_chunk<float>(const float* __restrict__ row, int lo, int hi, Best& b) {
-    const int nvec = (hi - lo) >> 2;
-    const f32x4* vp = reinterpret_cast<const f32x4*>(row + lo);
-    constexpr int U = 4;
-    int k = threadIdx.x;
-    for (; k + (U - 1) * kAcceptThreads < nvec; k += U * kAcceptThreads) {
-        f32x4 r[U];
+        __syncthreads();
+        float M = s_max[0];
+        int any_nan = s_idx[0];
         #pragma unroll
-        for (int j = 0; j < U; ++j) r[j] = __builtin_nontemporal_load(vp + k + j * kAcceptThreads);
-        #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int i0 = lo + ((k + j * kAcceptThreads) << 2);
-            #pragma unroll
-            for (int e = 0; e < 4; ++e) offer(b, r[j][e], i0 + e);
+        for (int k = 1; k < TH / kWave; ++k) {
+            M = fmaxf(M, s_max[k]);
+            any_nan |= s_idx[k];
         }
-    }
-    for (; k < nvec; k += kAcceptThreads) {
-        const f32x4 r = __builtin_nontemporal_load(vp + k);
-        const int i0 = lo + (k << 2);
+        if (any_nan) {
+            Best b{NEG, kNoIndex};
+            #pragma unroll
+            for (int j = 0; j < KR; ++j)
+                if (j < mine) vec_offer<T>(v[j], lo + (t + j * TH) * EPV, b);
+            return block_best(b, scratch);
+        }
+        int idx = kNoIndex;
+        if (m == M) {                                   // this thread holds the max (or has nothing and M = -inf)
+            #pragma unroll
+            for (int j = KR - 1; j >= 0; --j) {
+                if (j < mine) {
+                    const int k = vec_first<T>(v[j], M);
+                    idx = k < EPV ? lo + (t + j * TH) * EPV + k : idx;
+                }
+            }
+        }
+        __syncthreads();                                // every wave has read s_max / s_idx
+        idx = wave_min_i32(idx);
+        if ((t & 63) == 0) s_idx[t >> 6] = idx;
+        __syncthreads();
         #pragma unroll
-        for (int e = 0; e < 4; ++e) offer(b, r[e], i0 + e);
+        for (int k = 0; k < TH / kWave; ++k) idx = min(idx, s_idx[k]);
+        return Best{M, idx};
     }
-    for (int i = lo + (nvec << 2) + threadIdx.x; i < hi; i += kAcceptThreads) offer(b, row[i], i);
+    Best b{NEG, kNoIndex};
+    u32x4 cur[KB], nxt[KB];
+    auto load = [&](u32x4 (&dst)[KB], int j0) {
+        #pragma unroll
+        for (int j = 0; j < KB; ++j) dst[j] = __builtin_nontemporal_load(vp + min(t + (j0 + j) * TH, vlast));
+    };
+    auto scan = [&](const u32x4 (&src)[KB], int j0) {
+        #pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            if (j0 + j < mine) {
+                // per vector: its max, and only when that beats the thread's best (or
+                // nothing is recorded yet), the first position holding it
+                const float m = vec_max<T>(src[j], NEG);
+                const int i0 = lo + (t + (j0 + j) * TH) * EPV;
+                if (m != m) {
+                    vec_offer<T>(src[j], i0, b);
+                } else if (m > b.v || b.i == kNoIndex) {
+                    const int k = vec_first<T>(src[j], m);
+                    if (k < EPV) {                      // (a vector of quiet NaNs only finds nothing)
+                        b.v = m;
+                        b.i = i0 + k;
+                    }
+                }
+            }
+        }
+    };
+    load(cur, 0);
+    load(nxt, KB);
+    if (set_n > 0 && t < kWave) set_out = tree_set_wave(set_p, set_n);
+    for (int j0 = 0; j0 < mine; j0 += 2 * KB) {
+        scan(cur, j0);
+        if (j0 + 2 * KB < mine) load(cur, j0 + 2 * KB);
+        scan(nxt, j0 + KB);
+        if (j0 + 3 * KB < mine) load(nxt, j0 + 3 * KB);
+    }
+    return block_best(b, scratch);
 }
 
 // Scalar fallback for rows that are not 16-byte aligned.
 template <typename T>
-__device__ __forceinline__ void scan_scalar(const T* __restrict__ row, int lo, int hi, Best& b) {
+__device__ __forceinline__ Best chunk_best_scalar(const T* __restrict__ row, int lo, int hi, Best* scratch,
+                                                  int set_p, int set_n, uint64_t& set_out) {
+    if (set_n > 0 && threadIdx.x < kWave) set_out = tree_set_wave(set_p, set_n);
+    Best b{-__builtin_inff(), kNoIndex};
     for (int i = lo + threadIdx.x; i < hi; i += kAcceptThreads) {
         float v;
         if constexpr (sizeof(T) == 2) v = bf16_bits_to_f32(row[i]);
         else v = row[i];
         offer(b, v, i);
     }
+    return block_best(b, scratch);
 }
 
 struct AcceptArgs {
@@ -284,7 +399,7 @@ struct AcceptArgs {
 
 // Workgroup `blk` of the argmax + walk launch (one 256-thread workgroup per
 // (row, chunk); the sequence's last arriver merges and walks).
-template <typename T>
+template <typename T, int PATHS = 0>
 __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk) {
     __shared__ Best scratch[kAcceptThreads / kWave];
     __shared__ unsigned long long s_key[JF_MAX_NODES];
@@ -296,10 +411,16 @@ __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk)
     const int lo = c * a.chunk_len;
     const int hi = min(a.vocab, lo + a.chunk_len);
 
-    Best best{-__builtin_inff(), kNoIndex};
-    if (a.aligned) scan_chunk<T>(rp, lo, hi, best);
-    else scan_scalar<T>(rp, lo, hi, best);
-    best = block_best(best, scratch);
+    // The walk's node entries are requested before the scan by every workgroup, so
+    // the last one to finish already holds them. When the call builds the ancestor
+    // sets and the tree has at most 64 nodes, wave 0 builds them from the parents
+    // while the scan's loads are in flight (pointer doubling across its lanes).
+    NodeIn nd = load_node(b, a.N, a.parent, a.draft, a.anc_out ? nullptr : a.anc);
+    const bool wave_sets = a.anc_out != nullptr && a.N <= kWave;
+    uint64_t early_set = 0;
+    const int set_n = wave_sets ? a.N : 0;
+    const Best best = a.aligned ? chunk_best<T, PATHS>(rp, lo, hi, scratch, nd.p, set_n, early_set)
+                                : chunk_best_scalar<T>(rp, lo, hi, scratch, nd.p, set_n, early_set);
 
     // publish the chunk winner; the sequence's last workgroup to finish goes on
     const int per_seq = a.N * a.chunks;
@@ -332,9 +453,8 @@ __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk)
     __syncthreads();
     if (!last) return;
 
-    // every load of the final phase at once: this thread's node and up to 4
-    // chunk keys per pass (one pass covers N * C <= 1024)
-    NodeIn nd = load_node(b, a.N, a.parent, a.draft, a.anc_out ? nullptr : a.anc);
+    // every load of the final phase at once: up to 4 chunk keys per thread and
+    // pass (one pass covers N * C <= 1024)
     const uint64_t* pk = a.partial + (size_t)b * per_seq;
     const int u = threadIdx.x;
     if (u < a.N) s_key[u] = 0ull;
@@ -359,7 +479,18 @@ __device__ __forceinline__ void accept_logits_body(const AcceptArgs& a, int blk)
         a.next_tokens[(size_t)b * a.N + u] = nx;
     }
     __syncthreads();
-    if (a.anc_out) {
+    if (wave_sets) {
+        // built during the scan (wave 0 holds node u in lane u); written out as well
+        if (u < a.N) {
+            nd.a[0] = early_set;
+            a.anc_out[((size_t)b * a.N + u) * kAncWords] = early_set;
+            #pragma unroll
+            for (int k = 1; k < kAncWords; ++k) {
+                nd.a[k] = 0ull;
+                a.anc_out[((size_t)b * a.N + u) * kAncWords + k] = 0ull;
+            }
+        }
+    } else if (a.anc_out) {
         // the ancestor sets from the parent array (pointer doubling in LDS), written out as well
         const auto sets = tree_sets_lds(nd.p, a.N);
         if (u < a.N) {
