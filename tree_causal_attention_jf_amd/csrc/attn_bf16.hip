@@ -81,8 +81,9 @@ struct AttnArgs {
     uint16_t* out;
     float* lse;
     int* counters;     // [items]                       zero between calls
-    float* part_ml;    // [items][splits][RB][2]        (m in log2 units, l)
-    float* part_o;     // [items][splits] x [RB][D]     unnormalised, fragment-major (part_off)
+    float* part_ml;    // [items][splits][RB][4]        (m in log2 units, l, row scale r, unused)
+    float* part_o;     // [items][splits] x [RB][D]     unnormalised: fp32 fragment-major (part_off) with one
+                       //                               key group, else fp16 of O / r (half_off)
     uint32_t part_ml_bytes, part_o_bytes;
     int B, N, Hq, Hkv, G, num_pages, max_pages, max_prefix;
     int rows;          // G * N
@@ -261,6 +262,40 @@ __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* 
             }
         }
     }
+}
+
+// The tree tiles of a workgroup that runs the tree alone (its own split) in a
+// one-round ring, requested before anything else: their addresses depend on
+// no loaded value (the tree's K/V are the separate [B, N, Hkv, D] arrays). Wave
+// w moves tree tile w into ring slot w, only the transfers that hold tree keys
+// (a transfer that straddles the tree's end re-reads its last key); the value
+// rows of skipped transfers are zeroed, so that their zero weights multiply
+// finite values (key rows are left as they are: their scores are masked
+// before they are used). The caller waits with vmcnt(0) before the products.
+template <int D>
+__device__ __forceinline__ void issue_tree_tiles(const uint16_t* kt, const uint16_t* vt, int N, int Hkv, int b,
+                                                 int kvh, int nt, uint32_t ring0, char* ring, int w, int lane) {
+    using Gm = Geo<D>;
+    if (w >= nt) return;                                      // wave-uniform
+    const int t0 = w * kKeyTile;
+    const int nrows = min(kKeyTile, N - t0);
+    const int rsub = lane / Gm::CPR, pc = lane % Gm::CPR;
+    const uint32_t buf = ring0 + w * Gm::BUF_BYTES;
+    #pragma unroll
+    for (int ii = 0; ii < Gm::XFER_PER_TILE; ++ii) {
+        const bool isv = ii >= Gm::KB_PER_TILE;
+        const int row0 = (isv ? ii - Gm::KB_PER_TILE : ii) * Gm::ROWS_PER_KB;
+        if (row0 < nrows) {                                   // uniform
+            const int row = min(row0 + rsub, nrows - 1);
+            const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+            const uint16_t* gp = (isv ? vt : kt) + (((long)b * N + t0 + row) * Hkv + kvh) * D + c * 8;
+            dma16(__builtin_amdgcn_readfirstlane(buf + ii * 1024), gp);
+        }
+    }
+    const int zr0 = (nrows + Gm::ROWS_PER_KB - 1) / Gm::ROWS_PER_KB * Gm::ROWS_PER_KB;
+    char* vz = ring + w * Gm::BUF_BYTES + Gm::TILE_BYTES + zr0 * Gm::ROW_BYTES;
+    const int zbytes = (kKeyTile - zr0) * Gm::ROW_BYTES;
+    for (int off = lane * 16; off < zbytes; off += kWave * 16) *reinterpret_cast<u32x4*>(vz + off) = u32x4{0, 0, 0, 0};
 }
 
 // Wait until at most `pending` later rounds of this wave's transfers are in flight.
@@ -462,12 +497,59 @@ __device__ __forceinline__ uint32_t part_off(int r, int c) {
         return (uint32_t)(r * D + c * 4);
 }
 
+// Byte offset, inside one split's [RB][D] fp16 partial, of the 16 bytes that
+// thread `part` of row r's TPR threads (consecutive lanes) writes in its k-th
+// store: chunks 2k * TPR + part and (2k + 1) * TPR + part of the row (4 values
+// each). One store instruction puts a row's TPR threads side by side, so with
+// TPR = 8 it writes the row's whole 128-byte lines.
+template <int D, int TPR>
+__device__ __forceinline__ uint32_t half_off(int r, int part, int k) {
+    return (uint32_t)(r * (D * 2) + (k * TPR + part) * 16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;            // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ f32x4 unpack_f16x4(uint32_t w0, uint32_t w1) {
+    return f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xffffu)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xffffu)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
+}
+
+// Largest value over each aligned group of TPR (4 or 8) consecutive lanes, in
+// every lane of the group (DPP quad permutations, then the half-row mirror).
+template <int TPR>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(TPR == 4 || TPR == 8, "row groups of 4 or 8 lanes");
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad1032>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad2301>(__float_as_uint(v))));
+    if constexpr (TPR == 8) v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v))));
+    return v;
+}
+
+// OR of a value over the whole wave (DPP inside rows of 16, then readlane).
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+    v |= dpp_u32<kDppQuad1032>(v);
+    v |= dpp_u32<kDppQuad2301>(v);
+    v |= dpp_u32<kDppRowHalfMirror>(v);
+    v |= dpp_u32<kDppRowMirror>(v);
+    return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) | __builtin_amdgcn_readlane((int)v, 16) |
+                      __builtin_amdgcn_readlane((int)v, 32) | __builtin_amdgcn_readlane((int)v, 48));
+}
+
 // Workgroup `bid` of an attention grid of `nblk` workgroups (the attention
 // launch, or the attention part of the fused verification launch).
 template <int D, int RW, int KW, int RPW>
 __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const unsigned bid, const unsigned nblk) {
     using Gm = Geo<D>;
     constexpr bool kFragPart = KW == 1;              // split partial layout (part_off)
+    // With key groups the merged partial is written as fp16 of O / r, r the row's
+    // largest |O| (values in [-1, 1]: no overflow, 2^-11 of r per value), half the
+    // bytes of fp32 for the last arriver to read
+    constexpr bool kHalfPart = KW > 1;
     constexpr int NW = RW * KW;
     constexpr int T = NW * 64;
     constexpr int RB = RW * 32 * RPW;                // rows per workgroup: RW waves x RPW blocks of 32
@@ -583,19 +665,28 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     constexpr int PPT = (kMaxPagesPerSplit + T - 1) / T;
     // with tree_split, the last split slot holds no prefix pages
     const bool tree_wg = a.tree_split && s == a.splits - 1;
+    // a one-round ring's tree-only workgroup requests its tree tiles first (when
+    // they all fit the round and live in the separate tree arrays)
+    const int n_tree_tiles = (a.N + kKeyTile - 1) / kKeyTile;
+    const bool early_tree = RING_R == 1 && tree_wg && !a.paged_tree && a.tree_len == nullptr && n_tree_tiles <= KW;
     const int p_begin = tree_wg ? 0 : s * pps;
     const int p_avail = tree_wg ? 0 : min(pps, a.max_pages - p_begin);
+    // Every load of the set-up is unconditional (an index past the end is clamped,
+    // an absent array replaced by prefix_len, a valid address) and its value is
+    // selected where it is used: the compiler then counts the loads exactly, and a
+    // wait for one of them never also waits for every load issued after it.
     int L = a.prefix_len[b];
-    int nb = a.tree_len ? a.tree_len[b] : a.N;
+    const int nb_raw = *(a.tree_len ? a.tree_len + b : a.prefix_len + b);
     // when this launch builds the ancestor words itself: the parent of node `lane`
     // (trees of at most 64 nodes: every wave builds them alone) or of node tid
     const int par_idx = a.N <= kWave ? lane : tid;
-    const int par_own = (a.parent_sets && par_idx < a.N) ? a.parent_sets[(long)b * a.N + par_idx] : -1;
+    const int par_raw = *(a.parent_sets ? a.parent_sets + (long)b * a.N + min(par_idx, a.N - 1) : a.prefix_len + b);
     int pid[PPT];
     #pragma unroll
     for (int k = 0; k < PPT; ++k) {
         const int i = tid + k * T;
-        pid[k] = (i < p_avail) ? a.block_table[(long)b * a.max_pages + p_begin + i] : 0;
+        pid[k] = *(p_avail > 0 ? a.block_table + (long)b * a.max_pages + p_begin + min(i, p_avail - 1)
+                               : a.prefix_len + b);
     }
     // rows past the end read node 0 (a valid address): the loads stay unconditional,
     // so the compiler's wait for the ancestor words does not have to cover the Q
@@ -615,13 +706,23 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
         #pragma unroll
         for (int c = 0; c < DCH; ++c) qreg[blk][c] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * c));
     }
+    // (the tree tiles go out after the set-up loads: a wait for one of those loads
+    // then never has to wait for the tiles too, which are newer)
+    if (early_tree)
+        issue_tree_tiles<D>(a.kt, a.vt, a.N, a.Hkv, b, kvh, n_tree_tiles,
+                            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)ring), ring, w, lane);
+    int nb = a.tree_len ? nb_raw : a.N;
+    const int par_own = (a.parent_sets && par_idx < a.N) ? par_raw : -1;
     bool bad = (L < 0 || L > a.max_prefix);
     if (bad) L = 0;
     if (nb < 0 || nb > a.N) {                       // a bad tree length: every row of the sequence is NaN
         bad = true;
         nb = a.N;
     }
-    if (rb * RB >= nb * a.G) return;                // uniform: no row of the block is a node of the tree
+    if (rb * RB >= nb * a.G) {                      // uniform: no row of the block is a node of the tree
+        if (early_tree) wait_vm<0>();               // (never with early tree tiles; kept safe regardless)
+        return;
+    }
     // rows of nodes past the tree's length are not computed into the output
     #pragma unroll
     for (int blk = 0; blk < RPW; ++blk) {
@@ -674,23 +775,21 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
 
     if (tid < kAncWords) s_union[tid] = 0;
     __syncthreads();
-    // union of the block's ancestor sets: OR over the wave's 32 rows (both half-waves
-    // hold the same rows; rows past the end hold zero), then one LDS atomic per word
-    // and wave instead of one per row
-    if (has_tree && kw == 0) {
+    // union of the block's ancestor sets, for the words the tree has: OR over the
+    // wave's rows (DPP, no LDS; both half-waves hold the same rows and rows past the
+    // end hold zero), then one LDS atomic per word and wave. Tree tiles requested
+    // early need no union (every tile is run).
+    if (has_tree && kw == 0 && !early_tree) {
         #pragma unroll
         for (int k = 0; k < kAncWords; ++k) {
-            uint64_t u = ancw[0][k];
-            #pragma unroll
-            for (int blk = 1; blk < RPW; ++blk) u |= ancw[blk][k];
-            uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
-            #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) {
-                lo |= __shfl_xor(lo, o);
-                hi |= __shfl_xor(hi, o);
+            if (k * 64 < a.N) {                         // uniform
+                uint64_t u = ancw[0][k];
+                #pragma unroll
+                for (int blk = 1; blk < RPW; ++blk) u |= ancw[blk][k];
+                const unsigned long long word = ((unsigned long long)wave_or_u32((uint32_t)(u >> 32)) << 32) |
+                                                wave_or_u32((uint32_t)u);
+                if (lane == 0 && word) atomicOr(&s_union[k], word);
             }
-            const unsigned long long word = ((unsigned long long)hi << 32) | lo;
-            if (lane == 0 && word) atomicOr(&s_union[k], word);
         }
     }
     int my_bad = 0;
@@ -734,7 +833,12 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     // ---- tile list: prefix tiles, then the non-empty tree tiles
     const int n_pre = (tok_end - tok_begin + kKeyTile - 1) / kKeyTile;
     int tree_list = 0, n_tree = 0;   // up to 4 tile ids, 2 bits each
-    if (has_tree) {
+    if (early_tree) {
+        // every tree tile, in order, as issued (a tile no row has an ancestor in
+        // contributes zero weights)
+        tree_list = 0xe4;
+        n_tree = n_tree_tiles;
+    } else if (has_tree) {
         for (int tt = 0; tt * kKeyTile < a.N; ++tt) {
             if (s_union[tt]) {
                 tree_list |= tt << (2 * n_tree);
@@ -818,8 +922,9 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                                     s_tpages, tree_tok0);
         } else {
             __syncthreads();      // every wave is done with the previous round
-            issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl, ring0,
-                                w * DPR, lane, s_tpages, tree_tok0);
+            if (!(early_tree && r == 0))
+                issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl,
+                                    ring0, w * DPR, lane, s_tpages, tree_tok0);
             wait_vm<0>();
             __syncthreads();
         }
@@ -882,7 +987,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
             }
             if (h2f == 0) {
                 const u32x2 ml = {__float_as_uint(bad ? NANF : sb.m), __float_as_uint(bad ? NANF : l_tot)};
-                st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
+                st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 16, ml);
             }
         }
         if (n_act == 1) return;
@@ -952,11 +1057,23 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
         const uint32_t psplit = ((uint32_t)item * a.splits + s) * RB;
         const uint32_t pr = psplit + rl;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
+        static_assert(CPT % 2 == 0, "fp16 partials pair a thread's chunks");
+        float r = 0.f;
         #pragma unroll
-        for (int c = 0; c < CPT; ++c) st16(ro, (psplit * D + part_off<D, kFragPart>(rl, c * TPR + part)) * 4, acc[c]);
+        for (int c = 0; c < CPT; ++c)
+            r = fmaxf(r, fmaxf(fmaxf(fabsf(acc[c][0]), fabsf(acc[c][1])), fmaxf(fabsf(acc[c][2]), fabsf(acc[c][3]))));
+        r = group_max<TPR>(r);
+        const float rinv = r > 0.f ? 1.f / r : 0.f;
+        #pragma unroll
+        for (int k = 0; k < CPT / 2; ++k) {
+            const f32x4 x = acc[2 * k] * rinv, y = acc[2 * k + 1] * rinv;
+            const u32x4 h = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(y[0], y[1]),
+                             pack_f16x2(y[2], y[3])};
+            st16(ro, psplit * (D * 2) + half_off<D, TPR>(rl, part, k), __builtin_bit_cast(f32x4, h));
+        }
         if (part == 0) {
-            const u32x2 ml = {__float_as_uint(bad ? NANF : M), __float_as_uint(bad ? NANF : Ls)};
-            st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 8, ml);
+            const f32x4 ml = {bad ? NANF : M, bad ? NANF : Ls, r, 0.f};
+            st16(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 16, ml);
         }
     }
 
@@ -975,6 +1092,81 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     if (!s_last) return;
 
     {
+        if constexpr (kHalfPart) {
+        constexpr int TPR = T / RB;                // threads per row
+        constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread (CPT / 2 16-byte loads per split)
+        // splits per batch: every split's loads at once within the in-flight budget
+        constexpr int INFLIGHT = NW <= 4 ? 64 : 32;
+        constexpr int SB0 = INFLIGHT / (CPT / 2 + 1) > 1 ? INFLIGHT / (CPT / 2 + 1) : 1;
+        constexpr int SB = SB0 > 16 ? 16 : SB0;
+        const int rl = tid / TPR, part = tid % TPR;
+        const int grow = rb * RB + rl;
+        const uint32_t base = (uint32_t)item * a.splits * RB;        // + slot * RB
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
+        const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
+        const bool out_ok = grow < a.rows && grow / a.G < nb_e;
+        const int gnode = out_ok ? grow / a.G : 0, ghead = kvh * a.G + (out_ok ? grow % a.G : 0);
+        float M = NEG;
+        f32x4 acc[CPT];
+        #pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float Ls = 0.f;
+        for (int sp0 = 0; sp0 < n_act; sp0 += SB) {
+            u32x4 v[SB][CPT / 2];
+            f32x4 ml[SB];
+            #pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int kk = sp0 + j;
+                if (kk < n_act) {                      // uniform: slots past the last split load nothing
+                    const int slot = (a.tree_split && kk >= n_pre_e) ? a.splits - 1 : kk;
+                    const uint32_t ps = base + (uint32_t)slot * RB;
+                    #pragma unroll
+                    for (int k = 0; k < CPT / 2; ++k)
+                        v[j][k] = __builtin_bit_cast(u32x4, ld16(ro, ps * (D * 2) + half_off<D, TPR>(rl, part, k)));
+                    ml[j] = ld16(rml, (ps + rl) * 16);
+                } else {
+                    #pragma unroll
+                    for (int k = 0; k < CPT / 2; ++k) v[j][k] = u32x4{0u, 0u, 0u, 0u};
+                    ml[j] = f32x4{NEG, 0.f, 0.f, 0.f};
+                }
+            }
+            float mb = NEG;
+            #pragma unroll
+            for (int j = 0; j < SB; ++j) mb = fmaxf(mb, ml[j][0]);
+            const float Mn = fmaxf(M, mb);
+            const float Mn_use = (Mn == NEG) ? 0.f : Mn;
+            const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                          // M = -inf -> 0
+            Ls *= sc;
+            #pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] *= sc;
+            #pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                if (sp0 + j < n_act) {                 // uniform: no work for slots past the last split
+                    const float wgt = __builtin_amdgcn_exp2f(ml[j][0] - Mn_use);
+                    Ls += wgt * ml[j][1];
+                    const float wr = wgt * ml[j][2];                                      // weight x row scale
+                    #pragma unroll
+                    for (int k = 0; k < CPT / 2; ++k) {
+                        acc[2 * k] += wr * unpack_f16x4(v[j][k][0], v[j][k][1]);
+                        acc[2 * k + 1] += wr * unpack_f16x4(v[j][k][2], v[j][k][3]);
+                    }
+                }
+            }
+            M = Mn;
+        }
+        if (out_ok) {
+            const float inv = 1.f / Ls;
+            uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + part * 4;
+            #pragma unroll
+            for (int c = 0; c < CPT; ++c) {                   // acc[c] is chunk c * TPR + part
+                const u32x2 o = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
+                                 pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+                *reinterpret_cast<u32x2*>(op + 4 * TPR * c) = o;
+            }
+            if (a.lse && part == 0)
+                a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
+        }
+        } else {
         constexpr int TPR = T / RB;                // threads per row
         constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread
         constexpr int CB = CPT < 16 ? CPT : 16;    // chunks per pass over the splits
@@ -1010,7 +1202,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                         #pragma unroll
                         for (int c = 0; c < CB; ++c)
                             v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
-                        ml[j] = ld8(rml, (ps + rl) * 8);
+                        ml[j] = ld8(rml, (ps + rl) * 16);
                     } else {
                         #pragma unroll
                         for (int c = 0; c < CB; ++c) v[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1048,6 +1240,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                 if (a.lse && part == 0 && c0 == 0)
                     a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
             }
+        }
         }
     }
 }
@@ -1188,8 +1381,9 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
         p.off_cnt = 0;
         p.fill_bytes = p.items > kMaxCounters ? align256((size_t)(p.items - kMaxCounters) * 4) : 0;
         p.off_ml = kCounterBytes + p.fill_bytes;
-        p.off_o = p.off_ml + align256((size_t)p.items * splits * p.rb * 2 * 4);
-        p.bytes = p.off_o + align256((size_t)p.items * splits * p.rb * s.D * 4);
+        p.off_o = p.off_ml + align256((size_t)p.items * splits * p.rb * 4 * 4);
+        // fp16 partials with key groups (four-wave plans), fp32 without
+        p.bytes = p.off_o + align256((size_t)p.items * splits * p.rb * s.D * (p.kw > 1 ? 2 : 4));
     }
     return p;
 }
