@@ -32,6 +32,14 @@ made by:
     rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- python bench.py --profile-steps 20
     rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- python bench.py --profile-steps 20
     python bench.py --summarize-pmc F W
+The profile run also reads [4, 256, 151936] bf16 logits once with the
+acceptance kernel, a second kernel of known bytes for the FETCH_SIZE factor.
+
+Per-workload summaries in profiles/ (each file records its command):
+    rocprofv3 --kernel-trace --stats -d D -o run --output-format csv -- python bench.py --only NAME --no-cpu-baseline
+    python bench.py --summarize-stats D NAME
+    rocprofv3 --pmc <MFMA_COUNTERS> -d D -o run --output-format csv -- python bench.py --only NAME --no-cpu-baseline --profile-reps 2
+    python bench.py --summarize-mfma D NAME KERNEL AVERAGE_US
 """
 
 from __future__ import annotations
@@ -75,6 +83,15 @@ def parse():
                     help="run a 256 MiB copy (counter calibration), then this many eager steps, and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --profile-steps into the traffic summary")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "LABEL"),
+                    help="turn a rocprofv3 --kernel-trace --stats run into profiles/kernel_stats_LABEL.txt")
+    ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC_DIR", "LABEL", "KERNEL", "DURATION_US"),
+                    help="turn a rocprofv3 --pmc run of the MFMA counters into profiles/KERNEL_LABEL_mfma.txt "
+                         "(KERNEL: a substring of the kernel name; DURATION_US: its average duration)")
+    ap.add_argument("--command", default="",
+                    help="with --summarize-*: the profiler command line to record in the summary")
+    ap.add_argument("--profile-reps", type=int, default=0,
+                    help="sub-workloads replay each graph this many times (short runs under a profiler)")
     ap.add_argument("--only", default=None,
                     help="comma-separated subset of: step (the headline), " + ", ".join(SUBS))
     ap.add_argument("--separate", action="store_true",
@@ -123,14 +140,26 @@ def summarize_pmc(fetch_dir, write_dir, config):
     copy_kib = COPY_BYTES / 1024
 
     def copy_kernel(per):
-        # the calibration copy is the only dispatch moving ~COPY_BYTES
-        cands = [(n, max(v)) for n, v in per.items() if "copy" in n.lower() or "elementwise" in n.lower()]
+        # the calibration copy (a device-to-device tensor copy: the runtime's copy
+        # kernel) is the dispatch of that kernel moving the most bytes
+        cands = [(n, max(v)) for n, v in per.items() if "copybuffer" in n.lower()]
+        if not cands:
+            cands = [(n, max(v)) for n, v in per.items() if "copy" in n.lower()]
         n, v = max(cands, key=lambda t: t[1])
         return n, v
 
     cf_name, cf = copy_kernel(fetch)
     cw_name, cw = copy_kernel(write)
     f_fac, w_fac = copy_kib / cf, copy_kib / cw
+    # the acceptance kernel over [4, 256, 151936] bf16 logits reads each logit once
+    acc = [(n, v) for n, v in fetch.items() if "accept_logits_kernel" in n]
+    acc_line = "#   (no acceptance calibration in this run)"
+    if acc:
+        an, av = max(acc, key=lambda t: max(t[1]))
+        acc_kib = max(av)
+        logit_kib = 4 * 256 * 151936 * 2 / 1024
+        acc_line = (f"#   second calibration: acceptance over [4,256,151936] bf16 logits ({logit_kib:.0f} KiB read once) "
+                    f"shows FETCH_SIZE {acc_kib:.0f} KiB: factor {logit_kib / acc_kib:.4f}")
     lines = [f"# HBM traffic of the verification kernel (attention + acceptance), workload {config}",
              "# made by:",
              f"#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o run --output-format csv -- "
@@ -141,6 +170,7 @@ def summarize_pmc(fetch_dir, write_dir, config):
              f"# calibration: a {COPY_BYTES >> 20} MiB copy reads FETCH_SIZE {cf:.0f} KiB and "
              f"WRITE_SIZE {cw:.0f} KiB per dispatch",
              f"#   ({cf_name[:60]}); scale factors fetch {f_fac:.4f}, write {w_fac:.4f}",
+             acc_line,
              "# kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled bytes/dispatch"]
     attn = None
     for name in sorted(set(fetch) & set(write)):
@@ -159,6 +189,78 @@ def summarize_pmc(fetch_dir, write_dir, config):
               f"write_factor: {w_fac:.6f}",
               f"source_sha256: {source_digest()}"]
     out = traffic_file(config)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print(f"wrote {out}")
+
+
+def _stats_rows(d):
+    paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    assert paths, f"no kernel_stats.csv under {d}"
+    rows = []
+    for path in paths:
+        with open(path) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_stats(d, label, command):
+    """profiles/kernel_stats_LABEL.txt from a rocprofv3 --kernel-trace --stats run."""
+    lines = [f"# Kernel durations, rocprofv3 kernel trace of one bench.py run: {label}",
+             "# command (from the repository root; cd /tmp && export TMPDIR=/tmp for the profiler's scratch files):",
+             f"#   {command}" if command else "#   (command not given)",
+             f"#   python bench.py --summarize-stats <dir> {label}",
+             "# kernel | calls | average us | min us | max us | share of GPU time"]
+    for r in sorted(_stats_rows(d), key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        if "fill" in name.lower() or "elementwise" in name.lower() or "distribution" in name.lower():
+            name = "torch fill / random / elementwise (inputs and workspace set-up): " + name[:40]
+        lines.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}%")
+    out = os.path.join(ROOT, "profiles", f"kernel_stats_{label}.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print(f"wrote {out}")
+
+
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(d, label, kernel, duration_us, command):
+    """profiles/<kernel>_<label>_mfma.txt from a rocprofv3 --pmc run of MFMA_COUNTERS."""
+    per = {}
+    name = None
+    for c in MFMA_COUNTERS:
+        for n, v in read_counter_csv(d, c).items():
+            if kernel in n:
+                per.setdefault(c, []).extend(v)
+                name = n
+    assert name is not None, f"no dispatch of {kernel} in {d}"
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    simds, xcds = 1024, 8
+    mfma_cyc = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    gpu_cyc = avg["GRBM_GUI_ACTIVE"] / xcds
+    clock = gpu_cyc / (duration_us * 1e3)
+    short = kernel.replace("<", "_").replace(">", "").replace(", ", "_").replace(",", "_").replace(" ", "")
+    lines = [f"# MFMA counters, workload {label}, kernel {name}, {len(per['SQ_INSTS_MFMA'])} dispatches, "
+             "averages per dispatch",
+             "# command (from the repository root; cd /tmp && export TMPDIR=/tmp first):",
+             f"#   {command}" if command else "#   (command not given)",
+             f"#   python bench.py --summarize-mfma <dir> {label} '{kernel}' {duration_us}"]
+    lines += [f"{k}: {avg[k]:.0f}" for k in sorted(avg)]
+    lines += ["# SQ_VALU_MFMA_BUSY_CYCLES is 32 x SQ_INSTS_MFMA (32-cycle 32x32x16 bf16 MFMA), summed over 1024 SIMDs",
+              f"mfma_busy_cycles_per_simd: {mfma_cyc:.0f}",
+              f"# GRBM_GUI_ACTIVE is summed over the 8 XCDs: busy GPU cycles per XCD {gpu_cyc:.0f}",
+              f"mfma_busy_fraction_of_gpu_cycles: {mfma_cyc / gpu_cyc:.3f}",
+              f"valu_per_mfma: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}",
+              f"lds_bank_conflict_fraction: {avg['SQ_LDS_BANK_CONFLICT'] / max(1.0, avg['SQ_LDS_IDX_ACTIVE']):.3f}",
+              f"# clock under load: busy cycles per XCD / the kernel's average duration ({duration_us} us, kernel trace)",
+              f"clock_GHz: {clock:.2f}",
+              f"mfma_busy_fraction_at_2400MHz: {mfma_cyc / (duration_us * 1e3 * 2.4):.3f}"]
+    out = os.path.join(ROOT, "profiles", f"{short}_{label}_mfma.txt")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -239,9 +341,14 @@ def plan_graph_chunks(K, per):
     return plan
 
 
+REPS_OVERRIDE = 0   # --profile-reps: every graph replayed this many times instead
+
+
 def time_graph(fn_list, reps, stream):
     """Capture fn_list (callables) back to back in one graph, replay `reps`
     times between HIP events on `stream`; returns ms per callable."""
+    if REPS_OVERRIDE:
+        reps = REPS_OVERRIDE
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for f in fn_list:
@@ -582,6 +689,16 @@ def run_step(args, jf, W, stream):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        # second calibration: acceptance over [4, 256, 151936] bf16 logits, which reads
+        # every logit once (plus a few KB of tree data and chunk keys)
+        cal_logits = torch.randn((4, 256, 151936), device="cuda").to(torch.bfloat16)
+        cal_parent = torch.arange(-1, 255, dtype=torch.int32, device="cuda").repeat(4, 1).contiguous()
+        cal_draft = torch.zeros((4, 256), dtype=torch.int32, device="cuda")
+        cal_anc, _, _ = jf.build_ancestor_mask(cal_parent)
+        for _ in range(3):
+            jf.tree_accept(cal_parent, cal_anc, cal_draft, logits=cal_logits)
+        torch.cuda.synchronize()
+        del cal_logits
         with torch.cuda.stream(stream):
             for i in range(args.profile_steps):
                 steps[i % len(sets)]()
@@ -733,6 +850,15 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config)
         return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.command)
+        return
+    if args.summarize_mfma:
+        d, label, kernel, dur = args.summarize_mfma
+        summarize_mfma(d, label, kernel, float(dur), args.command)
+        return
+    global REPS_OVERRIDE
+    REPS_OVERRIDE = args.profile_reps
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
