@@ -70,3 +70,59 @@ def test_fewer_steps_than_input_sets_is_one_short_graph():
     assert bench.plan_graph_chunks(20, 40) == [(0, 20)]
     assert bench.plan_graph_chunks(40, 40) == [(0, 40)]
     assert bench.plan_graph_chunks(95, 40) == [(0, 40), (40, 40), (80, 15)]
+
+
+def test_acceptance_calibration_is_reported_beside_the_copy(tmp_path, monkeypatch, capsys):
+    copy_kib = bench.COPY_BYTES / 1024
+    logit_kib = 4 * 256 * 151936 * 2 / 1024
+    _write_counters(tmp_path / "F", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", copy_kib / 2),
+                                                    # a bigger elementwise kernel must not be taken for the copy
+                                                    ("void at::native::vectorized_elementwise_kernel<4>", 4 * copy_kib),
+                                                    ("void jf::accept_logits_kernel<unsigned short, 2>(jf::AcceptArgs)",
+                                                     logit_kib / 2),
+                                                    (VERIFY, 100.0)])
+    _write_counters(tmp_path / "W", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib), (VERIFY, 10.0)])
+    monkeypatch.setattr(bench, "traffic_file", lambda config: str(tmp_path / "traffic.txt"))
+    bench.summarize_pmc(str(tmp_path / "F"), str(tmp_path / "W"), "c1_chain16")
+    text = (tmp_path / "traffic.txt").read_text()
+    assert "fetch_factor: 2.000000" in text
+    assert "factor 2.0000" in text                      # acceptance: logits read once show at half
+    assert bench.read_traffic("c1_chain16")[0] == pytest.approx((100 * 2 + 10) * 1024, rel=1e-6)
+
+
+def test_stats_and_mfma_summaries(tmp_path, monkeypatch):
+    d = tmp_path / "kt"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs",
+                                           "Percentage"])
+        w.writeheader()
+        w.writerow(dict(Name=VERIFY, Calls=10, TotalDurationNs=155000, AverageNs=15500, MinNs=15000, MaxNs=16000,
+                        Percentage=90.0))
+        w.writerow(dict(Name="jf::ancestor_mask_kernel", Calls=10, TotalDurationNs=30000, AverageNs=3000,
+                        MinNs=2900, MaxNs=3100, Percentage=10.0))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    bench.summarize_stats(str(d), "step", "rocprofv3 ... -- python3 bench.py --only step")
+    text = (tmp_path / "profiles" / "kernel_stats_step.txt").read_text()
+    lines = [l for l in text.splitlines() if not l.startswith("#")]
+    assert lines[0].startswith(VERIFY) and "| 15.50 |" in lines[0]           # largest total first
+    assert "--only step" in text
+    # MFMA: 32 busy cycles per MFMA over 1024 SIMDs; GRBM over 8 XCDs
+    rows = [("tree_attn_bf16_kernel<128, 8, 1, 1>", {"SQ_INSTS_MFMA": 1024 * 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 32000,
+                                                     "SQ_BUSY_CYCLES": 1, "SQ_INSTS_VALU": 6 * 1024 * 1000,
+                                                     "SQ_LDS_BANK_CONFLICT": 0, "SQ_LDS_IDX_ACTIVE": 5,
+                                                     "GRBM_GUI_ACTIVE": 8 * 64000})]
+    m = tmp_path / "mfma"
+    m.mkdir()
+    with open(m / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, cs in rows:
+            for c, v in cs.items():
+                w.writerow({"Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    bench.summarize_mfma(str(m), "budget256", "tree_attn_bf16_kernel<128, 8, 1, 1>", 26.6667, "cmd")
+    text = (tmp_path / "profiles" / "tree_attn_bf16_kernel_128_8_1_1_budget256_mfma.txt").read_text()
+    assert "mfma_busy_fraction_of_gpu_cycles: 0.500" in text
+    assert "valu_per_mfma: 6.00" in text
+    assert "clock_GHz: 2.40" in text
