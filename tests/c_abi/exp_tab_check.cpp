@@ -1,9 +1,11 @@
-// Accuracy of the tree-construction kernel's table exponential (exp_tab.h,
+// Accuracy of the tree-construction kernel's table exponentials (exp_tab.h,
 // the same source the kernel compiles), on the CPU against the C library's
 // exp. The table is filled with the C library's exp2, as the kernel fills it
-// with the device library's. Prints the largest error in ulps of the result
-// (normal results) and in subnormal steps (subnormal results), and the
-// number of points checked.
+// with the device library's. exp_tab over its whole range: the largest error
+// in ulps of the result (normal results) and in subnormal steps (subnormal
+// results). exp_tab_nonpos over x <= 0: the largest relative error for
+// -40 <= x <= 0 and for -708 <= x < -40, and its special inputs (NaN, -inf and
+// x <= -746 give 0, zero gives exactly 1). Prints the figures and the points checked.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -28,7 +30,23 @@ int main() {
         z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
         return z ^ (z >> 31);
     };
+    bool nonpos = false;
+    double rel_near = 0.0, rel_far = 0.0;
     auto check = [&](double x) {
+        if (nonpos) {
+            if (!(x <= 0.0)) return;
+            ++points;
+            const double ref = std::exp(x);
+            const double got = jf::exp_tab_nonpos(x, tab);
+            if (x >= -708.0) {
+                const double rel = std::fabs(got - ref) / ref;
+                double& slot = x >= -40.0 ? rel_near : rel_far;
+                if (rel > slot) slot = rel;
+            } else if (!(got <= 2.0 * ref + 1e-300)) {
+                rel_far = 1.0;                  // deep underflow: no more than twice the true value
+            }
+            return;
+        }
         const double ref = std::exp(x);
         const double got = jf::exp_tab(x, tab);
         ++points;
@@ -51,15 +69,31 @@ int main() {
             }
         }
     };
-    // a dense grid over the whole range, every table slot at many offsets, and random points
-    for (long i = 0; i <= 4000000; ++i) check(-745.0 + (709.0 + 745.0) * (double)i / 4000000.0);
-    for (int k = -256 * 1075; k <= 256 * 1023; k += 7)
-        for (int f = -3; f <= 3; ++f) check((double)k * (0.6931471805599453 / 256.0) + f * 1e-4);
-    for (int i = 0; i < 2000000; ++i) {
-        const double u = (double)(next() >> 11) * 0x1.0p-53;
-        check(-745.0 + 1454.0 * u);
-        check((u - 0.5) * 1e-3);            // around zero
+    // a dense grid over the whole range, every table slot at many offsets, and random
+    // points; then the same points (those <= 0) for exp_tab_nonpos, with the special
+    // inputs it reads (NaN and -inf give 0, the clamp at -746, zero gives 1)
+    for (int pass = 0; pass < 2; ++pass) {
+        nonpos = pass == 1;
+        for (long i = 0; i <= 4000000; ++i) check(-745.0 + (709.0 + 745.0) * (double)i / 4000000.0);
+        for (int k = -256 * 1075; k <= 256 * 1023; k += 7)
+            for (int f = -3; f <= 3; ++f) check((double)k * (0.6931471805599453 / 256.0) + f * 1e-4);
+        for (int i = 0; i < 2000000; ++i) {
+            const double u = (double)(next() >> 11) * 0x1.0p-53;
+            check(-745.0 + 1454.0 * u);
+            check((u - 0.5) * 1e-3);            // around zero
+        }
+        for (double x : {-745.5, -746.0, -746.5, -800.0, -1e300}) check(x);
     }
-    std::printf("points %ld max_ulp %.4f at x=%.17g max_subnormal_steps %.4f\n", points, max_ulp, worst, max_sub);
+    long special_bad = 0;
+    for (double x : {(double)NAN, -(double)INFINITY, -746.0, -1e300})
+        special_bad += jf::exp_tab_nonpos(x, tab) != 0.0;
+    special_bad += jf::exp_tab_nonpos(0.0, tab) != 1.0;
+    special_bad += jf::exp_tab_nonpos(-0.0, tab) != 1.0;
+    for (long i = 0; i <= 4000000; ++i) {                   // exp_tab_nonpos where the scan's terms live
+        nonpos = true;
+        check(-40.0 * (double)i / 4000000.0);
+    }
+    std::printf("points %ld max_ulp %.4f at x=%.17g max_subnormal_steps %.4f special_bad %ld nonpos_rel_near %.3e "
+                "nonpos_rel_far %.3e\n", points, max_ulp, worst, max_sub, special_bad, rel_near, rel_far);
     return 0;
 }

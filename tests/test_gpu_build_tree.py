@@ -107,6 +107,27 @@ def test_build_tree_nan_and_infinite_rows(jf):
     _compare(jf, z, 4, 8, None, what="NaN / inf rows")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_build_tree_signalling_nan_patterns(jf, dtype):
+    # NaNs with the quiet bit clear (the one input that makes a hardware max3 NaN),
+    # of both signs, some beside the row's largest values: they count as -inf
+    case = W.make_draft_logits_case(43, 2, 24, 40000, topk=4, max_path_nodes=8, dtype=dtype)
+    z = case.logits.clone()
+    if dtype == torch.bfloat16:
+        bits, pos, neg = z.view(torch.int16), 0x7F81, -127                   # 0x7f81, 0xff81
+    else:
+        bits, pos, neg = z.view(torch.int32), 0x7F800001, -8388607           # 0x7f800001, 0xff800001
+    rng = np.random.Generator(np.random.PCG64(43))
+    for b in range(2):
+        for r in range(0, 24, 3):
+            top = int(z[b, r].float().argmax())
+            bits[b, r, top] = pos                                            # the largest logit becomes NaN
+            for c in rng.choice(40000, size=5, replace=False):
+                bits[b, r, int(c)] = neg if c % 2 else pos
+            bits[b, r, min(top + 1, 39999)] = neg
+    _compare(jf, z, 4, 8, None, what=f"signalling NaN {dtype}")
+
+
 def test_build_tree_workspace_reused_across_shapes(jf):
     # the arrival counters clean themselves: calls of different shapes share one workspace
     big = W.make_draft_logits_case(31, 4, 64, 40000, topk=4, max_path_nodes=8)

@@ -163,31 +163,6 @@ __device__ __forceinline__ NodeIn load_node(int b, int N, const int32_t* __restr
 // Chunks of at most this many 16-byte vectors are scanned from registers.
 constexpr int kRegChunkVecs = 16 * kAcceptThreads;
 
-// bf16 pair in one dword -> the two values as fp32 (low half first)
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Largest of the EPV values in a 16-byte vector, folded into m with v_max3
-// (a quiet NaN is ignored; a signalling NaN makes the result NaN).
-template <typename T>
-__device__ __forceinline__ float vec_max(const u32x4 r, float m) {
-    if constexpr (sizeof(T) == 2) {
-        const float a = max3f(bf_hi(r[0]), bf_hi(r[1]), bf_hi(r[2]));
-        const float c = max3f(bf_hi(r[3]), bf_lo(r[0]), bf_lo(r[1]));
-        return max3f(max3f(bf_lo(r[2]), bf_lo(r[3]), a), c, m);
-    } else {
-        return max3f(max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2])),
-                     __uint_as_float(r[3]), m);
-    }
-}
-
-// Value e (0 .. EPV-1, in index order) of a 16-byte vector.
-template <typename T>
-__device__ __forceinline__ float vec_val(const u32x4 r, int e) {
-    if constexpr (sizeof(T) == 2) return (e & 1) ? bf_hi(r[e >> 1]) : bf_lo(r[e >> 1]);
-    else return __uint_as_float(r[e]);
-}
-
 // Position (0 .. EPV-1) of the first value equal to m in a vector, or EPV.
 template <typename T>
 __device__ __forceinline__ int vec_first(const u32x4 r, float m) {
@@ -204,36 +179,6 @@ __device__ __forceinline__ void vec_offer(const u32x4 r, int i0, Best& b) {
     constexpr int EPV = 16 / (int)sizeof(T);
     #pragma unroll
     for (int e = 0; e < EPV; ++e) offer(b, vec_val<T>(r, e), i0 + e);
-}
-
-// Wave-wide max / min without LDS: DPP steps inside each row of 16 lanes (quad
-// permutations, then the half-row and row mirrors), then the four row results
-// read with readlane. The result is the same in every lane (scalar).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad1032>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuad2301>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(v))));
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-__device__ __forceinline__ int wave_min_i32(int v) {
-    v = min(v, (int)dpp_u32<kDppQuad1032>((uint32_t)v));
-    v = min(v, (int)dpp_u32<kDppQuad2301>((uint32_t)v));
-    v = min(v, (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v));
-    v = min(v, (int)dpp_u32<kDppRowMirror>((uint32_t)v));
-    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 // The winner (largest value, smallest index; NaN never wins) of logits

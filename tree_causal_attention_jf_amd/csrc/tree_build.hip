@@ -16,19 +16,25 @@
 //     nodes is not expanded; growth stops at the budget or when nothing is left.
 //
 // One launch:
-//  1. workgroup (sequence b, row i, chunk c) streams one 32768-value chunk
-//     (16384 for fp32) of row i with 16-byte loads held in registers, and
-//     computes the chunk's largest logit m_c, s_c = sum exp(z - m_c) in fp64,
-//     and its topk keys (value, then smaller index); it publishes them with
-//     agent-scope atomic stores and arrives on the sequence's counter (two
-//     levels when the sequence has many workgroups). Only rows that can be
-//     expanded run: i < budget - 1.
-//  2. the sequence's last workgroup merges each row's chunks (logsumexp and
-//     topk), then one wave grows the tree: each selected node keeps one head
-//     (its best child not yet taken) in the registers of lane node % 64; each
-//     step takes the best head across the wave (DPP max of the fp64 scores,
-//     ties to the smaller parent id), appends it as the next node, advances
-//     its parent's head and gives the new node its first head.
+//  1. workgroup (sequence b, row i, chunk c) reads one 32768-value chunk
+//     (16384 for fp32) of row i, every 16-byte load in flight at once and held
+//     in registers, and makes three passes over it: each vector's largest value
+//     (v_max3); the fp64 sum of exp(z - m_t) against the thread's largest value
+//     m_t (a table exponential good to 4e-14, exact at 0); the thread's sorted
+//     top-k, fed only from vectors whose largest value reaches a lower bound on
+//     the chunk's k-th largest (the k-th largest thread maximum of a wave, the
+//     best such bound over the workgroup's waves). It publishes the chunk's
+//     largest logit m_c, sum exp(z - m_c) and top-k with agent-scope atomic
+//     stores and arrives on the sequence's counter (two levels when the sequence
+//     has many workgroups). Only rows that can be expanded run: i < budget - 1.
+//  2. the sequence's last workgroup merges each row's chunks (online logsumexp,
+//     top-k), grows the tree in batches (candidates sorted, the prefix the
+//     serial loop would take added at once; nodes kept in LDS), then one wave
+//     finishes node by node: each selected node keeps one head (its best child
+//     not yet taken) in the registers of lane node % 64; each step takes the
+//     best head across the wave (DPP max of the fp64 scores, ties to the smaller
+//     parent id), appends it as the next node, advances its parent's head and
+//     gives the new node its first head.
 // The arrival counters return to zero, so the workspace never needs clearing
 // again (the same counter region as the other entry points).
 #include "jf_common.h"
@@ -101,17 +107,10 @@ __device__ __forceinline__ void insert_sorted(K (&l)[KT], K x) {
 
 // ---------------------------------------------------------------- wave reductions (DPP inside rows of 16)
 
-constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
-}
-
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const uint32_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
@@ -136,10 +135,10 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 __device__ __forceinline__ uint32_t minu(uint32_t a, uint32_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = minu(v, dpp32<kDppQuad1032>(v));
-    v = minu(v, dpp32<kDppQuad2301>(v));
-    v = minu(v, dpp32<kDppRowHalfMirror>(v));
-    v = minu(v, dpp32<kDppRowMirror>(v));
+    v = minu(v, dpp_u32<kDppQuad1032>(v));
+    v = minu(v, dpp_u32<kDppQuad2301>(v));
+    v = minu(v, dpp_u32<kDppRowHalfMirror>(v));
+    v = minu(v, dpp_u32<kDppRowMirror>(v));
     const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
     const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
     return minu(minu(a, b), minu(c, d));
@@ -298,38 +297,47 @@ __device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, cons
 
 // ---------------------------------------------------------------- growth in batches
 
-// Exclusive prefix sum of x over the workgroup (kBuildThreads threads); *total
-// receives the sum. Holds barriers: every thread calls it.
-__device__ __forceinline__ int block_exclusive_sum(int x, int* s_tmp, int* total) {
-    const int t = threadIdx.x;
-    s_tmp[t] = x;
-    __syncthreads();
-    for (int off = 1; off < kBuildThreads; off <<= 1) {
-        const int y = t >= off ? s_tmp[t - off] : 0;
-        __syncthreads();
-        s_tmp[t] += y;
-        __syncthreads();
+// Workgroup scans with one barrier: shuffle-up steps inside each wave, then the
+// waves' totals through LDS. s_w has one slot per wave; every thread calls them
+// (they hold a barrier), and the caller passes a barrier before reusing s_w.
+__device__ __forceinline__ int block_exclusive_sum(int x, int* s_w, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = x;
+    #pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
     }
-    const int incl = s_tmp[t];
-    *total = s_tmp[kBuildThreads - 1];
+    if (lane == 63) s_w[w] = incl;
     __syncthreads();
-    return incl - x;
+    int before = 0, tot = 0;
+    #pragma unroll
+    for (int k = 0; k < kBuildThreads / 64; ++k) {
+        const int v = s_w[k];
+        tot += v;
+        before += k < w ? v : 0;
+    }
+    *total = tot;
+    return before + incl - x;
 }
 
 // Exclusive prefix maximum of x over the workgroup (-inf for thread 0).
-__device__ __forceinline__ double block_exclusive_max(double x, double* s_tmp) {
-    const int t = threadIdx.x;
-    s_tmp[t] = x;
-    __syncthreads();
-    for (int off = 1; off < kBuildThreads; off <<= 1) {
-        const double y = t >= off ? s_tmp[t - off] : -__builtin_inf();
-        __syncthreads();
-        s_tmp[t] = s_tmp[t] > y ? s_tmp[t] : y;
-        __syncthreads();
+__device__ __forceinline__ double block_exclusive_max(double x, double* s_w) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double incl = x;
+    #pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (lane >= o) incl = incl > y ? incl : y;
     }
-    const double excl = t > 0 ? s_tmp[t - 1] : -__builtin_inf();
+    if (lane == 63) s_w[w] = incl;
+    const double prev = __shfl_up(incl, 1);
     __syncthreads();
-    return excl;
+    double r = lane > 0 ? prev : -__builtin_inf();
+    #pragma unroll
+    for (int k = 0; k < kBuildThreads / 64; ++k)
+        if (k < w) r = r > s_w[k] ? r : s_w[k];
+    return r;
 }
 
 // Scores only fall along a path (log-probabilities are negative), so the serial
@@ -338,25 +346,22 @@ __device__ __forceinline__ double block_exclusive_max(double x, double* s_tmp) {
 // joined first, then the child's rank), the loop takes c_1, c_2, ... in that order
 // for as long as each c_i scores at least as well as the best child of the nodes
 // c_1 .. c_{i-1} have just become (a new node joins after every existing parent, so
-// on equal scores c_i still wins). One round sorts the candidates (bitonic, in LDS),
+// on equal scores c_i still wins). Grown nodes are kept in LDS (parent, token,
+// score) and written out by the caller, so no round waits on global stores.
+// One round sorts the candidates (bitonic, in LDS),
 // finds that prefix and grows it. Rounds go on while they add at least 4 nodes;
 // the serial loop then continues from the state left in LDS. Run by the whole
 // workgroup. Returns the nodes grown (>= 1 when nb >= 1).
 template <int KT>
 __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
                             const int* s_cnt, double* s_nsc, int* s_dep, int* s_r, double* c_sc, int* c_key,
-                            double* s_dtmp, int* s_itmp) {
-    const int t = threadIdx.x;
-    const int N = a.N;
-    int32_t* par = a.parent + (size_t)b * N;
-    int32_t* tok = a.token + (size_t)b * N;
-    double* sc = a.score ? a.score + (size_t)b * N : nullptr;
+                            double* s_dtmp, int* s_itmp, int* s_isum, int* s_par, int* s_tokn) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const double ninf = -__builtin_inf();
     if (nb < 1) return 0;
     if (t == 0) {
-        par[0] = -1;
-        tok[0] = -1;
-        if (sc) sc[0] = 0.0;
+        s_par[0] = -1;
+        s_tokn[0] = -1;
         s_nsc[0] = 0.0;
         s_dep[0] = 1;
     }
@@ -368,7 +373,7 @@ __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, co
         int cnt_t = 0;
         if (t < n && t < rows_live && s_dep[t] < a.cap) cnt_t = max(0, s_cnt[t] - s_r[t]);
         int M = 0;
-        const int off = block_exclusive_sum(cnt_t, s_itmp, &M);
+        const int off = block_exclusive_sum(cnt_t, s_isum, &M);
         if (M == 0) break;                                        // uniform
         for (int j = 0; j < cnt_t; ++j) {
             const int key = t * KT + s_r[t] + j;
@@ -377,51 +382,103 @@ __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, co
         }
         int P = 1;
         while (P < M) P <<= 1;
-        for (int i = M + t; i < P; i += kBuildThreads) {
-            c_sc[i] = ninf;
-            c_key[i] = 0x7fffffff;
-        }
         __syncthreads();
-        // bitonic sort into the loop's order: larger score first, then smaller key
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = t; i < P / 2; i += kBuildThreads) {
-                    const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-                    const double xs = c_sc[lo], ys = c_sc[hi];
-                    const int xk = c_key[lo], yk = c_key[hi];
-                    const bool y_first = ys > xs || (ys == xs && yk < xk);
-                    const bool down = (lo & size) == 0;               // this block sorts into the loop's order
-                    if (down ? y_first : !y_first) {
-                        c_sc[lo] = ys;
-                        c_sc[hi] = xs;
-                        c_key[lo] = yk;
-                        c_key[hi] = xk;
+        // bitonic sort into the loop's order: larger score first, then smaller key;
+        // afterwards thread t holds the t-th candidate in (my_sc, my_key)
+        double my_sc;
+        int my_key;
+        if (P <= kBuildThreads) {
+            // one candidate per thread, in registers: partners at stride < 64 are in the
+            // same wave (shuffles), strides 64 and 128 go through LDS between barriers
+            my_sc = t < M ? c_sc[t] : ninf;
+            my_key = t < M ? c_key[t] : 0x7fffffff;
+            for (int ls_size = 1; (1 << ls_size) <= P; ++ls_size) {
+                const bool down = (t & (1 << ls_size)) == 0;         // this block sorts into the loop's order
+                for (int ls = ls_size - 1; ls >= 0; --ls) {
+                    const int stride = 1 << ls;
+                    double ps;
+                    int pk;
+                    if (stride >= 64) {
+                        __syncthreads();
+                        c_sc[t] = my_sc;
+                        c_key[t] = my_key;
+                        __syncthreads();
+                        ps = c_sc[t ^ stride];
+                        pk = c_key[t ^ stride];
+                    } else {
+                        ps = __shfl_xor(my_sc, stride);
+                        pk = __shfl_xor(my_key, stride);
+                    }
+                    const bool p_first = ps > my_sc || (ps == my_sc && pk < my_key);
+                    // the lower position of the pair keeps the first of the two when sorting
+                    // into the loop's order, the second otherwise
+                    if (((t & stride) == 0) == down ? p_first : !p_first) {
+                        my_sc = ps;
+                        my_key = pk;
                     }
                 }
-                __syncthreads();
             }
+        } else {
+            for (int i = M + t; i < P; i += kBuildThreads) {
+                c_sc[i] = ninf;
+                c_key[i] = 0x7fffffff;
+            }
+            __syncthreads();
+            // in LDS. Pair i of a stage with stride < 128 stays in the 128-element block of
+            // the wave that owns it (i = 64w + lane + 256j lies in block w + 4j), and one
+            // wave's LDS accesses take effect in order: such stages follow one another with
+            // only a compiler barrier. A stage with stride >= 128 mixes blocks: barriers.
+            bool prev_wide = false;
+            for (int ls_size = 1; (1 << ls_size) <= P; ++ls_size) {
+                const int size = 1 << ls_size;
+                for (int ls = ls_size - 1; ls >= 0; --ls) {           // stride 2^ls (shifts, not divisions)
+                    const int stride = 1 << ls;
+                    const bool wide = stride >= 128;
+                    if (wide && !prev_wide) __syncthreads();
+                    for (int i = t; i < P / 2; i += kBuildThreads) {
+                        const int lo = ((i >> ls) << (ls + 1)) + (i & (stride - 1)), hi = lo + stride;
+                        const double xs = c_sc[lo], ys = c_sc[hi];
+                        const int xk = c_key[lo], yk = c_key[hi];
+                        const bool y_first = ys > xs || (ys == xs && yk < xk);
+                        const bool down = (lo & size) == 0;
+                        if (down ? y_first : !y_first) {
+                            c_sc[lo] = ys;
+                            c_sc[hi] = xs;
+                            c_key[lo] = yk;
+                            c_key[hi] = xk;
+                        }
+                    }
+                    if (wide) __syncthreads();
+                    else __builtin_amdgcn_wave_barrier();
+                    prev_wide = wide;
+                }
+            }
+            if (!prev_wide) __syncthreads();
+            my_sc = c_sc[t];
+            my_key = c_key[t];
         }
         // the prefix the serial loop would take: candidate i becomes node n + i
         const int m = min(M, nb - n);
         double cand = ninf, child = ninf;
         if (t < m) {
-            const int u = n + t, v = c_key[t] / KT;
-            cand = c_sc[t];
+            const int u = n + t, v = my_key / KT;
+            cand = my_sc;
             if (s_dep[v] + 1 < a.cap && u < rows_live && s_cnt[u] > 0) child = cand + s_lp[u * KT];
         }
         const double best_new = block_exclusive_max(child, s_dtmp);
-        if (t == 0) s_itmp[0] = m;
+        // k: the first position whose candidate scores below a new node's best child
+        const unsigned long long stop = __ballot(t < m && !(cand >= best_new));
+        if (lane == 0) s_itmp[w] = stop ? w * 64 + __builtin_ctzll(stop) : m;
         __syncthreads();
-        if (t < m && !(cand >= best_new)) atomicMin(&s_itmp[0], t);
-        __syncthreads();
-        const int k = s_itmp[0];
+        int k = m;
+        #pragma unroll
+        for (int q = 0; q < kBuildThreads / 64; ++q) k = min(k, s_itmp[q]);
         // grow them
         if (t < k) {
-            const int u = n + t, key = c_key[t], v = key / KT;
-            par[u] = v;
-            tok[u] = s_tok[key];
-            if (sc) sc[u] = c_sc[t];
-            s_nsc[u] = c_sc[t];
+            const int u = n + t, key = my_key, v = key / KT;
+            s_par[u] = v;
+            s_tokn[u] = s_tok[key];
+            s_nsc[u] = my_sc;
             s_dep[u] = s_dep[v] + 1;
             atomicMax(&s_r[v], key - v * KT + 1);
         }
@@ -435,7 +492,7 @@ __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, co
 // ---------------------------------------------------------------- the kernel
 
 template <typename T, int KT>
-__global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
+__global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4))) void tree_build_kernel(BuildArgs a) {
     using KO = KeyOf<T>;
     using K = typename KO::type;
     constexpr int EPV = 16 / (int)sizeof(T);                 // elements per 16-byte vector
@@ -443,7 +500,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     __shared__ __attribute__((aligned(16))) double s_lp[JF_MAX_NODES * KT];   // phase 1 reuses it for keys
     __shared__ int s_tok[JF_MAX_NODES * KT];
     __shared__ int s_cnt[JF_MAX_NODES];
-    __shared__ float s_m[kNW];
+    __shared__ float s_m[kNW], s_tau[kNW];
     __shared__ double s_s[kNW];
     __shared__ int s_last;
     __shared__ double s_exp2[256];                            // 2^(j/256) for exp_tab
@@ -452,8 +509,9 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     __shared__ int s_dep[JF_MAX_NODES], s_r[JF_MAX_NODES];
     __shared__ double c_sc[JF_MAX_NODES * KT];
     __shared__ int c_key[JF_MAX_NODES * KT];
-    __shared__ double s_dtmp[kBuildThreads];
-    __shared__ int s_itmp[kBuildThreads];
+    __shared__ double s_dtmp[kNW];
+    __shared__ int s_itmp[kNW], s_isum[kNW];
+    __shared__ int s_par[JF_MAX_NODES], s_tokn[JF_MAX_NODES];
     static_assert(sizeof(K) * kBuildThreads * KT <= sizeof(double) * JF_MAX_NODES * KT, "key scratch");
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -476,91 +534,147 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     if (t < 256) s_exp2[t] = exp2((double)t / 256.0);
     __syncthreads();
 
-    // ---- phase 1: one chunk of row i, four 16-byte vectors per thread at a time
-    // with the next four in flight. Per value: its key into this thread's sorted
-    // top-KT, and exp(z - M_t) into an fp64 sum, where the reference M_t moves up
-    // only when a value exceeds it by more than 512 (then the sum is rescaled), so
-    // no term overflows and no separate max pass is needed.
+    // ---- phase 1: one chunk of row i, kBuildVecs 16-byte vectors per thread, all
+    // requested at once and held in registers, then three passes over them:
+    //  (a) each vector's largest value (v_max3) and the thread's, m_t;
+    //  (b) sum exp(z - m_t) over every value in fp64 (NaN and -inf add 0);
+    //  (c) the thread's sorted top-KT, fed only from vectors whose largest value
+    //      reaches tau. tau is a lower bound on the chunk's KT-th largest value:
+    //      in each wave the KT-th largest of the 64 thread maxima (those are KT
+    //      distinct values of the chunk), the largest over the workgroup's waves.
+    // A signalling NaN is the one input that makes a v_max3 result NaN: a thread
+    // that holds one takes its maximum value by value and offers every vector.
     const T* rp = reinterpret_cast<const T*>(a.logits) + ((size_t)b * a.N + i) * a.vocab;
     const int lo = c * a.chunk_len;
     const int hi = min(a.vocab, lo + a.chunk_len);
-    constexpr int G = 4;                                        // vectors per group
-    auto load_group = [&](int g, u32x4 (&dst)[G]) {
+    constexpr float NEG = -__builtin_inff();
+    constexpr uint32_t kNegWord = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;   // -inf in each value of a word
+    u32x4 v[kBuildVecs];
+    if (a.aligned) {
+        // every load is issued (past the chunk: the row's last chunk re-reads its last
+        // vector), then vectors past the chunk are replaced by -inf
+        const u32x4* vp = reinterpret_cast<const u32x4*>(rp + lo);
+        const int nvec = (hi - lo) / EPV;                   // aligned: the chunk holds whole vectors
         #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int v = g * G + q;
-            const int e0 = (v * kBuildThreads + t) * EPV;       // chunk-local index of the vector
-            if (a.aligned) {
-                const u32x4* vp = reinterpret_cast<const u32x4*>(rp + lo);
-                dst[q] = (lo + e0 < hi) ? __builtin_nontemporal_load(vp + v * kBuildThreads + t) : u32x4{0, 0, 0, 0};
-            } else {
-                uint32_t wd[4] = {0, 0, 0, 0};
-                #pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const int idx = lo + e0 + e;
-                    uint32_t x = 0;
-                    if (idx < hi) {
-                        if constexpr (sizeof(T) == 2) x = (uint32_t)reinterpret_cast<const uint16_t*>(rp)[idx];
-                        else x = __float_as_uint(reinterpret_cast<const float*>(rp)[idx]);
+        for (int j = 0; j < kBuildVecs; ++j) v[j] = __builtin_nontemporal_load(vp + min(j * kBuildThreads + t, nvec - 1));
+        if (hi - lo < a.chunk_len) {
+            #pragma unroll
+            for (int j = 0; j < kBuildVecs; ++j)
+                if (j * kBuildThreads + t >= nvec) v[j] = u32x4{kNegWord, kNegWord, kNegWord, kNegWord};
+        }
+    } else {
+        #pragma unroll
+        for (int j = 0; j < kBuildVecs; ++j) {
+            const int e0 = (j * kBuildThreads + t) * EPV;       // chunk-local index of the vector
+            uint32_t wd[4] = {kNegWord, kNegWord, kNegWord, kNegWord};
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int idx = lo + e0 + e;
+                if (idx < hi) {
+                    if constexpr (sizeof(T) == 2) {
+                        const uint32_t x = (uint32_t)reinterpret_cast<const uint16_t*>(rp)[idx];
+                        wd[e >> 1] = (wd[e >> 1] & ~(0xffffu << (16 * (e & 1)))) | (x << (16 * (e & 1)));
+                    } else {
+                        wd[e] = __float_as_uint(reinterpret_cast<const float*>(rp)[idx]);
                     }
-                    if constexpr (sizeof(T) == 2) wd[e >> 1] |= x << (16 * (e & 1));
-                    else wd[e] = x;
                 }
-                dst[q] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            }
+            v[j] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        }
+    }
+    // (a)
+    float vm[kBuildVecs];
+    float m_t = NEG;
+    bool nan_t = false;
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) {
+        vm[j] = vec_max<T>(v[j], NEG);
+        nan_t |= vm[j] != vm[j];
+    }
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; j += 2) m_t = max3f(vm[j], vm[j + 1], m_t);
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) asm volatile("" : "+v"(v[j]));
+    if (nan_t) {
+        m_t = NEG;
+        #pragma unroll
+        for (int j = 0; j < kBuildVecs; ++j)
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float z = vec_val<T>(v[j], e);
+                if (z > m_t) m_t = z;                           // NaN never passes
+            }
+    }
+    // the wave's bound: KT rounds of the wave's largest thread maximum, one holder removed each round
+    float tau_w, m_w;
+    {
+        float x = m_t;
+        float mx = wave_max_f32(x);
+        m_w = mx;
+        #pragma unroll
+        for (int r = 1; r < KT; ++r) {
+            const unsigned long long hold = __ballot(x == mx);
+            if (lane == (int)__builtin_ctzll(hold)) x = NEG;
+            mx = wave_max_f32(x);
+        }
+        tau_w = mx;
+    }
+    if (lane == 0) {
+        s_m[w] = m_w;
+        s_tau[w] = tau_w;
+    }
+    // (b) against the thread's own largest value. (The vectors pass through an empty
+    // asm between passes so each pass unpacks them again instead of the compiler
+    // keeping 128 unpacked values live from the previous one.)
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) asm volatile("" : "+v"(v[j]));
+    // Vectors from `live` on lie past the row's end in every lane (the last chunk)
+    // and add nothing: skipped with a uniform branch.
+    const int live = ((hi - lo + EPV - 1) / EPV + kBuildThreads - 1) / kBuildThreads;
+    const double md = (m_t > NEG && m_t < __builtin_inff()) ? (double)m_t : 0.0;
+    double s_a = 0.0, s_b = 0.0;
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) {
+        if (j < live) {
+            #pragma unroll
+            for (int e = 0; e < EPV; e += 2) {
+                s_a += exp_tab_nonpos((double)vec_val<T>(v[j], e) - md, s_exp2);
+                s_b += exp_tab_nonpos((double)vec_val<T>(v[j], e + 1) - md, s_exp2);
             }
         }
-    };
+    }
+    double s_t = s_a + s_b;
+    asm volatile("" : "+v"(s_t));                           // summed here, not sunk past pass (c)
+    __syncthreads();
+    float m_c = s_m[0], tau = s_tau[0];
+    #pragma unroll
+    for (int k = 1; k < kNW; ++k) {
+        m_c = fmaxf(m_c, s_m[k]);
+        tau = fmaxf(tau, s_tau[k]);
+    }
+    tau = fmaxf(tau, -__FLT_MAX__);                             // z >= tau: neither NaN nor -inf
+    // (c)
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) asm volatile("" : "+v"(v[j]));
     K top[KT];
     #pragma unroll
     for (int j = 0; j < KT; ++j) top[j] = 0;
-    float M_t = -__builtin_inff();
-    double s_t = 0.0;
-    u32x4 cur[G], nxt[G];
-    load_group(0, cur);
-    #pragma unroll 1
-    for (int g = 0; g < kBuildVecs / G; ++g) {
-        if (g + 1 < kBuildVecs / G) load_group(g + 1, nxt);
-        #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int v = g * G + q;
-            float z[EPV];
-            bool ok[EPV];
-            float vmax = -__builtin_inff();
+    #pragma unroll
+    for (int j = 0; j < kBuildVecs; ++j) {
+        if (nan_t || vm[j] >= tau) {
+            u32x4 x = v[j];
+            asm volatile("" : "+v"(x));                         // unpacked here, not ahead of the branch
             #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                if constexpr (sizeof(T) == 2) z[e] = __uint_as_float((cur[q][e >> 1] >> (16 * (e & 1))) << 16);
-                else z[e] = __uint_as_float(cur[q][e]);
-                const int local = (v * kBuildThreads + t) * EPV + e;
-                ok[e] = (lo + local < hi) && z[e] > -__builtin_inff();   // NaN and -inf never enter
-                insert_sorted<K, KT>(top, ok[e] ? KO::make(z[e], local) : (K)0);
-                vmax = ok[e] ? fmaxf(vmax, z[e]) : vmax;
+                const float z = vec_val<T>(x, e);
+                if (z >= tau) insert_sorted<K, KT>(top, KO::make(z, (j * kBuildThreads + t) * EPV + e));
             }
-            if (vmax > M_t + 512.f) {                           // first values, or a far larger one
-                if (M_t > -__builtin_inff()) s_t *= exp((double)M_t - (double)vmax);
-                M_t = vmax;
-            }
-            const double md = (double)M_t;
-            #pragma unroll
-            for (int e = 0; e < EPV; ++e) s_t += ok[e] ? exp_tab((double)z[e] - md, s_exp2) : 0.0;
         }
-        #pragma unroll
-        for (int q = 0; q < G; ++q) cur[q] = nxt[q];
     }
-    // this thread's largest value
-    const float m_t = top[0] ? KO::value(top[0]) : -__builtin_inff();
-    // chunk max, then the chunk's sum rescaled to it
-    float m_w = m_t;
-    #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m_w = fmaxf(m_w, __shfl_xor(m_w, o));
     K* s_keys = reinterpret_cast<K*>(s_lp);
     #pragma unroll
     for (int j = 0; j < KT; ++j) s_keys[t * KT + j] = top[j];
-    if (lane == 0) s_m[w] = m_w;
-    __syncthreads();
-    float m_c = s_m[0];
-    #pragma unroll
-    for (int k = 1; k < kNW; ++k) m_c = fmaxf(m_c, s_m[k]);
-    double part = (M_t > -__builtin_inff() && s_t > 0.0) ? s_t * exp((double)M_t - (double)m_c) : 0.0;
+    double part = (m_t > NEG && s_t > 0.0) ? s_t * exp((double)m_t - (double)m_c) : 0.0;
     #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const unsigned long long u = (unsigned long long)__double_as_longlong(part);
@@ -622,7 +736,10 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
             if (closes) {
                 const int old = arrive(&a.seq_count[b]);
                 is_last = (old == expect - 1);
-                if (is_last) reset_counter(&a.seq_count[b]);
+                if (is_last) {
+                    reset_counter(&a.seq_count[b]);
+                    acquire_agent();                            // the records are then read with plain loads
+                }
             }
             s_last = is_last;
         }
@@ -633,30 +750,39 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     // ---- phase 2 (the sequence's last workgroup): each row's logsumexp and children
     const unsigned long long* rb = a.rec + (size_t)b * (a.N > 1 ? a.N - 1 : 1) * a.chunks * a.rec_words;
     if (t < rows_live) {
+        // row t: its chunks' records, CG at a time with every load in flight; the
+        // logsumexp runs online (the sum is rescaled when a chunk holds a larger max)
+        constexpr int RW = 2 + KT, CG = KT <= 4 ? 4 : 2;
         const unsigned long long* rr = rb + (size_t)t * a.chunks * a.rec_words;
         float m = -__builtin_inff();
-        for (int cc = 0; cc < a.chunks; ++cc) {
-            const unsigned long long w0 =
-                __hip_atomic_load(rr + (size_t)cc * a.rec_words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            m = fmaxf(m, __uint_as_float((uint32_t)w0));
-        }
-        int cnt = 0;
-        if (m > -__builtin_inff() && m < __builtin_inff()) {
-            double s = 0.0;
-            unsigned long long best[KT];
+        double s = 0.0;
+        unsigned long long best[KT];
+        #pragma unroll
+        for (int j = 0; j < KT; ++j) best[j] = 0;
+        for (int c0 = 0; c0 < a.chunks; c0 += CG) {
+            unsigned long long r[CG][RW];
             #pragma unroll
-            for (int j = 0; j < KT; ++j) best[j] = 0;
-            for (int cc = 0; cc < a.chunks; ++cc) {
-                const unsigned long long* rc = rr + (size_t)cc * a.rec_words;
-                const float mc = __uint_as_float((uint32_t)__hip_atomic_load(rc, __ATOMIC_RELAXED,
-                                                                             __HIP_MEMORY_SCOPE_AGENT));
-                const double scc = __longlong_as_double((long long)__hip_atomic_load(rc + 1, __ATOMIC_RELAXED,
-                                                                                     __HIP_MEMORY_SCOPE_AGENT));
-                if (mc > -__builtin_inff()) s += scc * exp((double)mc - (double)m);
+            for (int q = 0; q < CG; ++q) {
+                const unsigned long long* rc = rr + (size_t)min(c0 + q, a.chunks - 1) * a.rec_words;
+                #pragma unroll
+                for (int k = 0; k < RW; ++k) r[q][k] = rc[k];
+            }
+            #pragma unroll
+            for (int q = 0; q < CG; ++q) {
+                if (c0 + q >= a.chunks) break;
+                const float mc = __uint_as_float((uint32_t)r[q][0]);
+                const double scc = __longlong_as_double((long long)r[q][1]);
+                if (mc > -__builtin_inff()) {
+                    if (mc > m) {
+                        s = (m > -__builtin_inff() ? s * exp((double)m - (double)mc) : 0.0) + scc;
+                        m = mc;
+                    } else {
+                        s += scc * exp((double)mc - (double)m);
+                    }
+                }
                 #pragma unroll
                 for (int j = 0; j < KT; ++j) {
-                    const unsigned long long e = __hip_atomic_load(rc + 2 + j, __ATOMIC_RELAXED,
-                                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned long long e = r[q][2 + j];
                     const float ev = __uint_as_float((uint32_t)e);
                     const uint32_t etok = (uint32_t)(e >> 32);
                     // global key: value, then the smaller token id
@@ -666,6 +792,9 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
                     insert_sorted<unsigned long long, KT>(best, key);
                 }
             }
+        }
+        int cnt = 0;
+        if (m > -__builtin_inff() && m < __builtin_inff()) {
             const double lse = (double)m + log(s);
             #pragma unroll
             for (int j = 0; j < KT; ++j) {
@@ -680,7 +809,18 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     }
     __syncthreads();
     const int n0 = grow_batches<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt, s_nsc, s_dep, s_r, c_sc, c_key, s_dtmp,
-                                    s_itmp);
+                                    s_itmp, s_isum, s_par, s_tokn);
+    // the batches' nodes (the serial loop writes its own, all past n0)
+    {
+        int32_t* par = a.parent + (size_t)b * a.N;
+        int32_t* tok = a.token + (size_t)b * a.N;
+        double* sc = a.score ? a.score + (size_t)b * a.N : nullptr;
+        for (int v = t; v < n0; v += kBuildThreads) {
+            par[v] = s_par[v];
+            tok[v] = s_tokn[v];
+            if (sc) sc[v] = s_nsc[v];
+        }
+    }
     if (w == 0) grow_tree<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt, n0, s_nsc, s_dep, s_r);
 }
 
