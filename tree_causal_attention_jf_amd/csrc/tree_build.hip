@@ -19,7 +19,7 @@
 //  1. workgroup (sequence b, row i, chunk c) reads one 32768-value chunk
 //     (16384 for fp32) of row i, every 16-byte load in flight at once and held
 //     in registers, and makes three passes over it: each vector's largest value
-//     (v_max3); the fp64 sum of exp(z - m_t) against the thread's largest value
+//     (packed 16-bit maxima of bf16 patterns, v_max3 for fp32); the fp64 sum of exp(z - m_t) against the thread's largest value
 //     m_t (a table exponential good to 4e-14, exact at 0); the thread's sorted
 //     top-k, fed only from vectors whose largest value reaches a lower bound on
 //     the chunk's k-th largest (the k-th largest thread maximum of a wave, the
@@ -57,6 +57,16 @@ struct BuildArgs {
     unsigned long long* rec;    // [B][N-1][chunks][rec_words] chunk records (workspace)
     int N, vocab, chunks, chunk_len, topk, cap, groups, rec_words, aligned;
 };
+
+// ---------------------------------------------------------------- packed maxima
+
+typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
+
+// per-half signed 16-bit maximum (v_pk_max_i16)
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b)));
+}
 
 // ---------------------------------------------------------------- keys
 
@@ -167,7 +177,7 @@ __device__ __forceinline__ K wave_max_key(K v) {
 // s_lp / s_tok / s_cnt hold each expandable row's children (rows < rows_live).
 // Run by wave 0 alone.
 template <int KT>
-__device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
+__device__ __forceinline__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
                           const int* s_cnt, int n0 = 0, const double* s_nsc = nullptr, const int* s_dep = nullptr,
                           const int* s_r = nullptr) {
     const int lane = threadIdx.x;
@@ -297,17 +307,52 @@ __device__ void grow_tree(const BuildArgs& a, int b, int nb, int rows_live, cons
 
 // ---------------------------------------------------------------- growth in batches
 
-// Workgroup scans with one barrier: shuffle-up steps inside each wave, then the
-// waves' totals through LDS. s_w has one slot per wave; every thread calls them
-// (they hold a barrier), and the caller passes a barrier before reusing s_w.
+// Wave scans over DPP: shifts inside each row of 16 lanes (row_shr 1, 2, 4, 8),
+// then the row broadcasts (lane 15 of a row into the next row, lane 31 into the
+// upper half). A lane whose DPP source does not exist receives the identity.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143, kDppWaveShr1 = 0x138, kDppRowRor8 = 0x128;
+constexpr int kDppQuad3210 = 0x1b;
+
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xc, 0xf, false);
+    return x;
+}
+
+// v moved by a DPP control; lanes the control does not reach (no source, or a
+// row outside ROWS) get `fill`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64_fill(double v, double fill) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const unsigned long long f = (unsigned long long)__double_as_longlong(fill);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)f, (int)(uint32_t)u, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(f >> 32), (int)(uint32_t)(u >> 32), CTRL,
+                                                              ROWS, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_incl_max(double x) {
+    const double ni = -__builtin_inf();
+    x = maxd(x, dpp_f64_fill<kDppRowShr1, 0xf>(x, ni));
+    x = maxd(x, dpp_f64_fill<kDppRowShr2, 0xf>(x, ni));
+    x = maxd(x, dpp_f64_fill<kDppRowShr4, 0xf>(x, ni));
+    x = maxd(x, dpp_f64_fill<kDppRowShr8, 0xf>(x, ni));
+    x = maxd(x, dpp_f64_fill<kDppRowBcast15, 0xa>(x, ni));
+    x = maxd(x, dpp_f64_fill<kDppRowBcast31, 0xc>(x, ni));
+    return x;
+}
+
+// Workgroup scans with one barrier: a DPP scan inside each wave, then the waves'
+// totals through LDS. s_w has one slot per wave; every thread calls them (they
+// hold a barrier), and the caller passes a barrier before reusing s_w.
 __device__ __forceinline__ int block_exclusive_sum(int x, int* s_w, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = x;
-    #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_sum(x);
     if (lane == 63) s_w[w] = incl;
     __syncthreads();
     int before = 0, tot = 0;
@@ -324,20 +369,82 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int* s_w, int* total) 
 // Exclusive prefix maximum of x over the workgroup (-inf for thread 0).
 __device__ __forceinline__ double block_exclusive_max(double x, double* s_w) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double incl = x;
-    #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if (lane >= o) incl = incl > y ? incl : y;
-    }
+    const double incl = wave_incl_max(x);
     if (lane == 63) s_w[w] = incl;
-    const double prev = __shfl_up(incl, 1);
+    double r = dpp_f64_fill<kDppWaveShr1, 0xf>(incl, -__builtin_inf());   // the lane before (lane 0: -inf)
     __syncthreads();
-    double r = lane > 0 ? prev : -__builtin_inf();
     #pragma unroll
     for (int k = 0; k < kBuildThreads / 64; ++k)
-        if (k < w) r = r > s_w[k] ? r : s_w[k];
+        if (k < w) r = maxd(r, s_w[k]);
     return r;
+}
+
+// The value of lane (lane ^ 2^LS): DPP inside rows of 16 (quad permutations; the
+// half-row mirror then a quad reversal for 4; a rotation by 8), shuffles beyond.
+template <int LS>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    if constexpr (LS == 0) return dpp_u32<kDppQuad1032>(v);
+    else if constexpr (LS == 1) return dpp_u32<kDppQuad2301>(v);
+    else if constexpr (LS == 2) return dpp_u32<kDppQuad3210>(dpp_u32<kDppRowHalfMirror>(v));
+    else if constexpr (LS == 3) return dpp_u32<kDppRowRor8>(v);
+    else return (uint32_t)__shfl_xor((int)v, 1 << LS);
+}
+
+// A register bitonic sort of one candidate per thread (thread t ends up holding
+// the t-th in the loop's order: larger score first, then smaller key). Partners
+// at stride 2^LS < 64 are in the same wave (xor_lane); strides 64 and 128 go
+// through LDS between barriers. Branch-free compares (bitwise | and &), and the
+// strides are compile-time constants, so a step is a few DPP moves, compares
+// and selects.
+template <int LS>
+__device__ __forceinline__ void bitonic_step(double& sc, int& key, bool down, double* c_sc, int* c_key) {
+    const int t = threadIdx.x;
+    double ps;
+    int pk;
+    if constexpr (LS < 6) {
+        const unsigned long long u = (unsigned long long)__double_as_longlong(sc);
+        const uint32_t plo = xor_lane<LS>((uint32_t)u), phi = xor_lane<LS>((uint32_t)(u >> 32));
+        ps = __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
+        pk = (int)xor_lane<LS>((uint32_t)key);
+    } else {
+        __syncthreads();
+        c_sc[t] = sc;
+        c_key[t] = key;
+        __syncthreads();
+        ps = c_sc[t ^ (1 << LS)];
+        pk = c_key[t ^ (1 << LS)];
+    }
+    const bool p_first = (ps > sc) | ((ps == sc) & (pk < key));
+    // the lower position of the pair keeps the first of the two when sorting into
+    // the loop's order, the second otherwise
+    const bool take = ((((t >> LS) & 1) == 0) == down) ? p_first : !p_first;
+    sc = take ? ps : sc;
+    key = take ? pk : key;
+}
+
+template <int LS>
+__device__ __forceinline__ void bitonic_steps(double& sc, int& key, bool down, double* c_sc, int* c_key) {
+    bitonic_step<LS>(sc, key, down, c_sc, c_key);
+    if constexpr (LS > 0) bitonic_steps<LS - 1>(sc, key, down, c_sc, c_key);
+}
+
+// levels 2^1 .. P (P <= 2^MAXL, a power of two; uniform). MAXL 6 sorts inside one
+// wave (no LDS, no barrier); MAXL 8 sorts the workgroup's 256 threads.
+template <int MAXL>
+__device__ __forceinline__ void bitonic_sort_reg(double& sc, int& key, int P, double* c_sc, int* c_key) {
+    const int t = threadIdx.x;
+#define JF_BITONIC_LEVEL(L) \
+    if constexpr ((L) <= MAXL) \
+        if ((1 << (L)) <= P) bitonic_steps<(L) - 1>(sc, key, (t & (1 << (L))) == 0, c_sc, c_key);
+    JF_BITONIC_LEVEL(1)
+    JF_BITONIC_LEVEL(2)
+    JF_BITONIC_LEVEL(3)
+    JF_BITONIC_LEVEL(4)
+    JF_BITONIC_LEVEL(5)
+    JF_BITONIC_LEVEL(6)
+    JF_BITONIC_LEVEL(7)
+    JF_BITONIC_LEVEL(8)
+#undef JF_BITONIC_LEVEL
 }
 
 // Scores only fall along a path (log-probabilities are negative), so the serial
@@ -353,9 +460,9 @@ __device__ __forceinline__ double block_exclusive_max(double x, double* s_w) {
 // the serial loop then continues from the state left in LDS. Run by the whole
 // workgroup. Returns the nodes grown (>= 1 when nb >= 1).
 template <int KT>
-__device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
+__device__ __forceinline__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, const double* s_lp, const int* s_tok,
                             const int* s_cnt, double* s_nsc, int* s_dep, int* s_r, double* c_sc, int* c_key,
-                            double* s_dtmp, int* s_itmp, int* s_isum, int* s_par, int* s_tokn) {
+                            double* s_dtmp, int* s_itmp, int* s_isum, int* s_par, int* s_tokn, int* s_ctl) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const double ninf = -__builtin_inf();
     if (nb < 1) return 0;
@@ -368,6 +475,66 @@ __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, co
     if (t < JF_MAX_NODES) s_r[t] = 0;
     __syncthreads();
     int n = 1;
+    // Rounds in which every grown node and every candidate fits one lane (n <= 64,
+    // M <= 64) run on wave 0 alone: the same steps with DPP scans, a one-wave
+    // register sort and ballots, no workgroup barrier (one wave's LDS accesses take
+    // effect in order). The other waves wait for them at one barrier.
+    if (w == 0) {
+        int done = 0;
+        while (n < nb && n <= 64) {
+            int cnt = 0;
+            if (lane < n && lane < rows_live && s_dep[lane] < a.cap) cnt = max(0, s_cnt[lane] - s_r[lane]);
+            const int incl = wave_incl_sum(cnt);
+            const int M = __builtin_amdgcn_readlane(incl, 63);
+            if (M == 0) {
+                done = 1;
+                break;
+            }
+            if (M > 64) break;                                    // a workgroup round
+            const int off = incl - cnt;
+            for (int j = 0; j < cnt; ++j) {
+                const int key = lane * KT + s_r[lane] + j;
+                c_sc[off + j] = s_nsc[lane] + s_lp[key];
+                c_key[off + j] = key;
+            }
+            __builtin_amdgcn_wave_barrier();
+            int P = 1;
+            while (P < M) P <<= 1;
+            double my_sc = lane < M ? c_sc[lane] : ninf;
+            int my_key = lane < M ? c_key[lane] : 0x7fffffff;
+            bitonic_sort_reg<6>(my_sc, my_key, P, nullptr, nullptr);
+            const int m = min(M, nb - n);
+            double cand = ninf, child = ninf;
+            const int u = n + lane, v = my_key / KT;
+            if (lane < m) {
+                cand = my_sc;
+                if (s_dep[v] + 1 < a.cap && u < rows_live && s_cnt[u] > 0) child = cand + s_lp[u * KT];
+            }
+            const double best_new = dpp_f64_fill<kDppWaveShr1, 0xf>(wave_incl_max(child), ninf);
+            const unsigned long long stop = __ballot(lane < m && !(cand >= best_new));
+            const int k = stop ? (int)__builtin_ctzll(stop) : m;
+            if (lane < k) {
+                s_par[u] = v;
+                s_tokn[u] = s_tok[my_key];
+                s_nsc[u] = my_sc;
+                s_dep[u] = s_dep[v] + 1;
+                atomicMax(&s_r[v], my_key - v * KT + 1);
+            }
+            __builtin_amdgcn_wave_barrier();
+            n += k;
+            if (k < 4) {
+                done = 1;
+                break;
+            }
+        }
+        if (lane == 0) {
+            s_ctl[0] = n;
+            s_ctl[1] = done;
+        }
+    }
+    __syncthreads();
+    n = s_ctl[0];
+    if (s_ctl[1]) return n;
     while (n < nb) {
         // candidates: node t (grown, expandable) offers its children r .. cnt-1
         int cnt_t = 0;
@@ -388,36 +555,10 @@ __device__ int grow_batches(const BuildArgs& a, int b, int nb, int rows_live, co
         double my_sc;
         int my_key;
         if (P <= kBuildThreads) {
-            // one candidate per thread, in registers: partners at stride < 64 are in the
-            // same wave (shuffles), strides 64 and 128 go through LDS between barriers
+            // one candidate per thread, in registers
             my_sc = t < M ? c_sc[t] : ninf;
             my_key = t < M ? c_key[t] : 0x7fffffff;
-            for (int ls_size = 1; (1 << ls_size) <= P; ++ls_size) {
-                const bool down = (t & (1 << ls_size)) == 0;         // this block sorts into the loop's order
-                for (int ls = ls_size - 1; ls >= 0; --ls) {
-                    const int stride = 1 << ls;
-                    double ps;
-                    int pk;
-                    if (stride >= 64) {
-                        __syncthreads();
-                        c_sc[t] = my_sc;
-                        c_key[t] = my_key;
-                        __syncthreads();
-                        ps = c_sc[t ^ stride];
-                        pk = c_key[t ^ stride];
-                    } else {
-                        ps = __shfl_xor(my_sc, stride);
-                        pk = __shfl_xor(my_key, stride);
-                    }
-                    const bool p_first = ps > my_sc || (ps == my_sc && pk < my_key);
-                    // the lower position of the pair keeps the first of the two when sorting
-                    // into the loop's order, the second otherwise
-                    if (((t & stride) == 0) == down ? p_first : !p_first) {
-                        my_sc = ps;
-                        my_key = pk;
-                    }
-                }
-            }
+            bitonic_sort_reg<8>(my_sc, my_key, P, c_sc, c_key);
         } else {
             for (int i = M + t; i < P; i += kBuildThreads) {
                 c_sc[i] = ninf;
@@ -511,7 +652,7 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ int c_key[JF_MAX_NODES * KT];
     __shared__ double s_dtmp[kNW];
     __shared__ int s_itmp[kNW], s_isum[kNW];
-    __shared__ int s_par[JF_MAX_NODES], s_tokn[JF_MAX_NODES];
+    __shared__ int s_par[JF_MAX_NODES], s_tokn[JF_MAX_NODES], s_ctl[2];
     static_assert(sizeof(K) * kBuildThreads * KT <= sizeof(double) * JF_MAX_NODES * KT, "key scratch");
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -536,14 +677,12 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
 
     // ---- phase 1: one chunk of row i, kBuildVecs 16-byte vectors per thread, all
     // requested at once and held in registers, then three passes over them:
-    //  (a) each vector's largest value (v_max3) and the thread's, m_t;
+    //  (a) each vector's largest value and the thread's, m_t;
     //  (b) sum exp(z - m_t) over every value in fp64 (NaN and -inf add 0);
     //  (c) the thread's sorted top-KT, fed only from vectors whose largest value
     //      reaches tau. tau is a lower bound on the chunk's KT-th largest value:
     //      in each wave the KT-th largest of the 64 thread maxima (those are KT
     //      distinct values of the chunk), the largest over the workgroup's waves.
-    // A signalling NaN is the one input that makes a v_max3 result NaN: a thread
-    // that holds one takes its maximum value by value and offers every vector.
     const T* rp = reinterpret_cast<const T*>(a.logits) + ((size_t)b * a.N + i) * a.vocab;
     const int lo = c * a.chunk_len;
     const int hi = min(a.vocab, lo + a.chunk_len);
@@ -582,20 +721,39 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
             v[j] = u32x4{wd[0], wd[1], wd[2], wd[3]};
         }
     }
-    // (a)
-    float vm[kBuildVecs];
+    // (a) bf16: packed 16-bit integer maxima of the bit patterns. Non-negative
+    // bf16 values order like their patterns and lie above every negative pattern,
+    // so when the thread's largest pattern is non-negative and not a NaN pattern it
+    // is the thread's largest value; otherwise (every value negative, or a NaN with
+    // the sign clear) the thread takes its maximum value by value. fp32: v_max3
+    // per vector (a signalling NaN, the one input that makes it NaN, sends the
+    // thread through the same value-by-value path).
     float m_t = NEG;
-    bool nan_t = false;
-    #pragma unroll
-    for (int j = 0; j < kBuildVecs; ++j) {
-        vm[j] = vec_max<T>(v[j], NEG);
-        nan_t |= vm[j] != vm[j];
+    bool exact_t = false;                                       // vectors are filtered value by value
+    uint32_t vmp[kBuildVecs];                                   // bf16: packed per-vector maxima
+    float vm[sizeof(T) == 2 ? 1 : kBuildVecs];                  // fp32: per-vector maxima
+    if constexpr (sizeof(T) == 2) {
+        #pragma unroll
+        for (int j = 0; j < kBuildVecs; ++j)
+            vmp[j] = pk_max_i16(pk_max_i16(v[j][0], v[j][1]), pk_max_i16(v[j][2], v[j][3]));
+        uint32_t tp = vmp[0];
+        #pragma unroll
+        for (int j = 1; j < kBuildVecs; ++j) tp = pk_max_i16(tp, vmp[j]);
+        const int mx = max((int)(int16_t)(tp & 0xffffu), (int)(int16_t)(tp >> 16));
+        exact_t = !(mx >= 0 && mx <= 0x7f80);
+        m_t = __uint_as_float((uint32_t)mx << 16);
+    } else {
+        #pragma unroll
+        for (int j = 0; j < kBuildVecs; ++j) {
+            vm[j] = vec_max<T>(v[j], NEG);
+            exact_t |= vm[j] != vm[j];
+        }
+        #pragma unroll
+        for (int j = 0; j < kBuildVecs; j += 2) m_t = max3f(vm[j], vm[j + 1], m_t);
     }
     #pragma unroll
-    for (int j = 0; j < kBuildVecs; j += 2) m_t = max3f(vm[j], vm[j + 1], m_t);
-    #pragma unroll
     for (int j = 0; j < kBuildVecs; ++j) asm volatile("" : "+v"(v[j]));
-    if (nan_t) {
+    if (exact_t) {
         m_t = NEG;
         #pragma unroll
         for (int j = 0; j < kBuildVecs; ++j)
@@ -659,9 +817,25 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     K top[KT];
     #pragma unroll
     for (int j = 0; j < KT; ++j) top[j] = 0;
+    // bf16 with tau > 0: a vector holds a value >= tau exactly when a packed max
+    // against (tau's pattern - 1) in both halves changes it (negative patterns lie
+    // below; a NaN pattern with the sign clear only adds a needless check)
+    const bool int_hits = sizeof(T) == 2 && tau > 0.f;
+    const uint32_t tt = ((__float_as_uint(tau) >> 16) - 1u) * 0x10001u;
     #pragma unroll
     for (int j = 0; j < kBuildVecs; ++j) {
-        if (nan_t || vm[j] >= tau) {
+        bool hit;
+        if constexpr (sizeof(T) == 2) {
+            if (int_hits) {
+                hit = pk_max_i16(vmp[j], tt) != tt;
+            } else {
+                const float mj = vec_max<T>(v[j], NEG);
+                hit = !(mj < tau);                              // a NaN maximum: check value by value
+            }
+        } else {
+            hit = !(vm[j] < tau);
+        }
+        if (exact_t || hit) {
             u32x4 x = v[j];
             asm volatile("" : "+v"(x));                         // unpacked here, not ahead of the branch
             #pragma unroll
@@ -674,7 +848,7 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     K* s_keys = reinterpret_cast<K*>(s_lp);
     #pragma unroll
     for (int j = 0; j < KT; ++j) s_keys[t * KT + j] = top[j];
-    double part = (m_t > NEG && s_t > 0.0) ? s_t * exp((double)m_t - (double)m_c) : 0.0;
+    double part = (m_t > NEG && s_t > 0.0) ? s_t * exp_tab_nonpos((double)m_t - (double)m_c, s_exp2) : 0.0;
     #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const unsigned long long u = (unsigned long long)__double_as_longlong(part);
@@ -774,10 +948,10 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
                 const double scc = __longlong_as_double((long long)r[q][1]);
                 if (mc > -__builtin_inff()) {
                     if (mc > m) {
-                        s = (m > -__builtin_inff() ? s * exp((double)m - (double)mc) : 0.0) + scc;
+                        s = (m > -__builtin_inff() ? s * exp_tab_nonpos((double)m - (double)mc, s_exp2) : 0.0) + scc;
                         m = mc;
                     } else {
-                        s += scc * exp((double)mc - (double)m);
+                        s += scc * exp_tab_nonpos((double)mc - (double)m, s_exp2);
                     }
                 }
                 #pragma unroll
@@ -809,7 +983,7 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     }
     __syncthreads();
     const int n0 = grow_batches<KT>(a, b, nb, rows_live, s_lp, s_tok, s_cnt, s_nsc, s_dep, s_r, c_sc, c_key, s_dtmp,
-                                    s_itmp, s_isum, s_par, s_tokn);
+                                    s_itmp, s_isum, s_par, s_tokn, s_ctl);
     // the batches' nodes (the serial loop writes its own, all past n0)
     {
         int32_t* par = a.parent + (size_t)b * a.N;
