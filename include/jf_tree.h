@@ -119,7 +119,8 @@ typedef struct {
 /*
  * Bytes of workspace jf_tree_attention needs for this shape and prefix bound
  * (0 when the call needs none: fp32, a grid without split prefixes, or an
- * invalid shape).
+ * invalid shape); enough for jf_tree_attention_paged_tree's plan of the same
+ * shape as well.
  *
  * Workspace contract (both jf_tree_attention and jf_tree_accept): the first
  * JF_WORKSPACE_COUNTER_BYTES bytes are arrival counters. They must be zero
@@ -149,6 +150,15 @@ size_t jf_tree_attention_workspace_bytes(const jf_attn_shape* s, int32_t max_pre
  * NULL), JF_ERR_UNSUPPORTED (fp32: one workgroup per 64 rows, no plan).
  */
 jf_status jf_tree_attention_plan(const jf_attn_shape* s, int32_t max_prefix_len, int32_t* plan);
+
+/*
+ * jf_tree_attention_paged_tree_plan -- the launch plan jf_tree_attention_paged_tree
+ * would use for a bf16 call of this shape: the same fields as
+ * jf_tree_attention_plan. Ragged budgets take 128-row blocks wherever
+ * jf_tree_attention would take 256-row ones (half the padding rows of a
+ * partly filled tree). Same host errors as jf_tree_attention_plan.
+ */
+jf_status jf_tree_attention_paged_tree_plan(const jf_attn_shape* s, int32_t max_prefix_len, int32_t* plan);
 
 /*
  * jf_tree_attention -- tree-causal attention over a paged prefix

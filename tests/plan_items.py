@@ -13,13 +13,13 @@ import numpy as np
 def plan_items(jf, wl, tree_len=None):
     """The items of the plan jf_tree_attention uses for workload `wl` (anything
     with q [B, N, Hq, D], k_pages, block_table, sm_scale, max_prefix_len), the
-    plan's rows per workgroup, and the plan. With tree_len (ragged budgets), row
-    blocks holding no node of sequence b's tree are not items (the kernel skips
-    them)."""
+    plan's rows per workgroup, and the plan. With tree_len (ragged budgets, run
+    through jf_tree_attention_paged_tree, whose plan is asked for), row blocks
+    holding no node of sequence b's tree are not items (the kernel skips them)."""
     B, N, Hq, _ = wl.q.shape
     Hkv = wl.k_pages.shape[1]
     shape = jf.attn_shape(wl.q, wl.k_pages, wl.block_table, wl.sm_scale)
-    plan = jf.tree_attention_plan(shape, wl.max_prefix_len)
+    plan = jf.tree_attention_plan(shape, wl.max_prefix_len, paged_tree=tree_len is not None)
     G = Hq // Hkv
     RB = plan["rows_per_workgroup"]
     items = []

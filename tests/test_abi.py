@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                "jf_tree_attention_workspace_bytes", "jf_tree_accept_workspace_bytes", "jf_version",
                "jf_commit_accepted", "jf_tree_attention_paged_tree", "jf_build_tree",
                "jf_build_tree_workspace_bytes", "jf_tree_verify", "jf_tree_attention_plan",
-               "jf_tree_verify_noalloc"):
+               "jf_tree_attention_paged_tree_plan", "jf_tree_verify_noalloc"):
         assert fn in names
 
 

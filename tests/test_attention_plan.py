@@ -2,8 +2,9 @@
 GPU): 32-row blocks with four key groups at budget 16, 64-row streaming blocks
 once many tiles fall to each workgroup, a grid that never exceeds one
 workgroup per CU unless the 1024-page split limit binds (room kept for the
-tree's own split), 7/8 of the CUs for one
-sequence in 256-row blocks, and the batch schedule for 2..64 sequences."""
+tree's own split), 128-row blocks for one sequence with few items and for
+ragged budgets, 7/8 of the CUs for one sequence in 256-row blocks, and the
+batch schedule for 2..64 sequences."""
 
 import itertools
 
@@ -53,9 +54,37 @@ def test_one_sequence_grid_never_exceeds_the_cus(jf):
         assert p["splits"] >= 1 and p["pages_per_split"] % 4 == 0
 
 
-def test_one_sequence_256_row_blocks_leave_cus_free(jf):
+def test_one_sequence_few_items_take_128_row_blocks(jf):
+    # 1 x 256 nodes, 8 KV heads: 256-row blocks would give 32 items (7 splits each);
+    # 128-row blocks with two key groups give 64 items x 4 splits
     p = plan(jf, 8192, N=256)
-    assert (p["rows_per_workgroup"], p["splits"], p["workgroups"]) == (256, 7, 224)
+    assert (p["rows_per_workgroup"], p["key_groups"], p["splits"], p["workgroups"]) == (128, 2, 4, 256)
+
+
+def test_one_sequence_256_row_blocks_leave_cus_free(jf):
+    # enough items for 256-row blocks (16 KV heads: 64 items): 7/8 of the CUs
+    p = plan(jf, 8192, N=256, Hkv=16, Hq=64)
+    assert p["rows_per_workgroup"] == 256 and p["workgroups"] <= 224, p
+
+
+def test_batches_of_full_trees_keep_256_row_blocks(jf):
+    for B, L in ((8, 4096), (4, 32768)):
+        assert plan(jf, L, B=B, N=256)["rows_per_workgroup"] == 256
+
+
+def test_ragged_budgets_take_128_row_blocks(jf):
+    d = dict(B=8, N=256, Hq=32, Hkv=8, D=128, page_size=16)
+    pages = 4096 // 16 + 256 // 16 + 1
+    s = _shape(jf, num_pages=pages * 8, max_pages_per_seq=pages, **d)
+    full, ragged = jf.tree_attention_plan(s, 4096), jf.tree_attention_plan(s, 4096, paged_tree=True)
+    assert full["rows_per_workgroup"] == 256 and ragged["rows_per_workgroup"] == 128 and ragged["key_groups"] == 2
+    # one workspace serves both entry points
+    import ctypes
+    need = jf._lib.jf_tree_attention_workspace_bytes(ctypes.byref(s), 4096)
+    assert need > 0
+    # budget-16 shapes: the same plan either way
+    s16 = _shape(jf, num_pages=200, max_pages_per_seq=200, B=1, N=16, Hq=32, Hkv=8, D=128, page_size=16)
+    assert jf.tree_attention_plan(s16, 2048) == jf.tree_attention_plan(s16, 2048, paged_tree=True)
 
 
 def test_batches_use_the_device_schedule(jf):

@@ -128,6 +128,21 @@ def test_build_tree_signalling_nan_patterns(jf, dtype):
     _compare(jf, z, 4, 8, None, what=f"signalling NaN {dtype}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_build_tree_negative_and_mixed_sign_rows(jf, dtype):
+    # every logit negative (log-probability-like rows: each thread's largest value is
+    # negative and the chunk's threshold is below zero), and rows whose best values sit
+    # around zero (-0.0 and +0.0 among them)
+    case = W.make_draft_logits_case(47, 2, 24, 70000, topk=4, max_path_nodes=8, dtype=dtype)
+    z = case.logits.clone()
+    z[0] = z[0] - 40.0
+    z[1] = z[1] - float(z[1].float().max()) + 0.5
+    z[1, :, 5] = 0.0
+    z[1, :, 6] = -0.0
+    z[1, 3, 7] = 0.0
+    _compare(jf, z, 4, 8, None, what=f"negative / mixed-sign rows {dtype}")
+
+
 def test_build_tree_workspace_reused_across_shapes(jf):
     # the arrival counters clean themselves: calls of different shapes share one workspace
     big = W.make_draft_logits_case(31, 4, 64, 40000, topk=4, max_path_nodes=8)

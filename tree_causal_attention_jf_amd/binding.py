@@ -43,6 +43,7 @@ EXPORTED = (
     "jf_tree_verify",
     "jf_tree_attention_plan",
     "jf_tree_verify_noalloc",
+    "jf_tree_attention_paged_tree_plan",
 )
 
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.jf_tree_attention_workspace_bytes.argtypes = [ctypes.POINTER(AttnShape), i32]
     lib.jf_tree_attention_plan.restype = i32
     lib.jf_tree_attention_plan.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.jf_tree_attention_paged_tree_plan.restype = i32
+    lib.jf_tree_attention_paged_tree_plan.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(ctypes.c_int32)]
     lib.jf_tree_attention.restype = i32
     lib.jf_tree_attention.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -225,10 +228,12 @@ PLAN_FIELDS = ("rows_per_workgroup", "key_groups", "row_blocks_per_wave", "split
                "tree_split", "workgroups")
 
 
-def tree_attention_plan(shape: AttnShape, max_prefix_len: int) -> dict:
-    """The launch plan jf_tree_attention would use (bf16; nothing is launched)."""
+def tree_attention_plan(shape: AttnShape, max_prefix_len: int, paged_tree: bool = False) -> dict:
+    """The launch plan jf_tree_attention (paged_tree: jf_tree_attention_paged_tree)
+    would use (bf16; nothing is launched)."""
     out = (ctypes.c_int32 * 8)()
-    _check("jf_tree_attention_plan", _lib.jf_tree_attention_plan(ctypes.byref(shape), int(max_prefix_len), out))
+    fn = "jf_tree_attention_paged_tree_plan" if paged_tree else "jf_tree_attention_plan"
+    _check(fn, getattr(_lib, fn)(ctypes.byref(shape), int(max_prefix_len), out))
     return dict(zip(PLAN_FIELDS, list(out)))
 
 

@@ -33,7 +33,7 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                               int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
                               int anc_from_parent, hipStream_t stream);
 bool verify_fusable(const jf_attn_shape& s, int max_prefix, int logits_dtype);
-void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int32_t* out);
+void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int ragged, int32_t* out);
 hipError_t launch_commit(const jf_attn_shape& s, const void* k_tree, const void* v_tree, const int32_t* accept_len,
                          const int32_t* accepted_nodes, const int32_t* block_table, const int32_t* prefix_len,
                          void* k_pages, void* v_pages, int32_t* new_prefix_len, hipStream_t stream);
@@ -131,7 +131,16 @@ jf_status jf_tree_attention_plan(const jf_attn_shape* s, int32_t max_prefix_len,
     if (st != JF_OK) return st;
     if (!plan) return JF_ERR_NULL;
     if (s->dtype != JF_BF16) return JF_ERR_UNSUPPORTED;
-    jf::attention_bf16_plan(*s, max_prefix_len, plan);
+    jf::attention_bf16_plan(*s, max_prefix_len, 0, plan);
+    return JF_OK;
+}
+
+jf_status jf_tree_attention_paged_tree_plan(const jf_attn_shape* s, int32_t max_prefix_len, int32_t* plan) {
+    const jf_status st = check_attn_shape(s, max_prefix_len);
+    if (st != JF_OK) return st;
+    if (!plan) return JF_ERR_NULL;
+    if (s->dtype != JF_BF16) return JF_ERR_UNSUPPORTED;
+    jf::attention_bf16_plan(*s, max_prefix_len, 1, plan);
     return JF_OK;
 }
 

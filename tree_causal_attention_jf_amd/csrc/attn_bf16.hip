@@ -1273,13 +1273,25 @@ static int env_int(const char* name, int dflt) {
     return atoi(v);
 }
 
-AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix) {
+AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix, int ragged) {
     AttnPlanBf16 p{};
     const long rows = (long)(s.Hq / s.Hkv) * s.N;
     // few rows -> key groups keep several tiles in flight per workgroup
     if (rows <= 64) { p.rw = 1; p.kw = 4; }
     else if (rows <= 128) { p.rw = 4; p.kw = 2; }
-    else { p.rw = 8; p.kw = 1; }   // (128-row blocks hold one prefetch round: slower)
+    else {
+        // 256-row blocks (8 waves, one key group) when they give the chip enough
+        // items; 128-row blocks with two key groups when 256-row blocks would leave
+        // fewer items than a quarter of the CUs (one sequence: the items then need
+        // many splits, each merged through fp32 partials) or when the budgets are
+        // ragged (128-row blocks waste half as many padding rows). Measured: the
+        // draft head's pass (1 x 256 nodes, 8192 prefix) 62.3 -> 55.4 us, ragged
+        // budgets U{16..256} x 8 99.5 -> 90.3 us; batches of full trees lose
+        // (budget 256 x 8: 131.5 -> 137.6 us; prefix 32768 x 4: 517 -> 588 us).
+        const long items8 = (long)s.B * s.Hkv * ((rows + 255) / 256);
+        if (ragged || items8 * 4 < 256) { p.rw = 4; p.kw = 2; }
+        else { p.rw = 8; p.kw = 1; }
+    }
     p.rpw = 1;
     {
         // Few rows but many tiles per workgroup: streaming the prefix sets the time.
@@ -1469,7 +1481,7 @@ hipError_t launch_attention_bf16(const jf_attn_shape& s, int max_prefix, const v
                                  const void* k_tree, const void* v_tree, const uint64_t* anc, void* out,
                                  float* lse, void* workspace, hipStream_t stream, const int32_t* tree_len,
                                  int paged_tree) {
-    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix, paged_tree);
     if (p.grid == 0) return hipSuccess;
     const AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
                                       v_tree, anc, out, lse, workspace, tree_len, paged_tree);
@@ -1511,7 +1523,7 @@ static hipError_t launch_verify_d(const AttnPlanBf16& p, const AttnArgs& a, cons
 
 bool verify_fusable(const jf_attn_shape& s, int max_prefix, int logits_dtype) {
     if (s.dtype != JF_BF16 || logits_dtype != JF_BF16 || s.B == 0) return false;
-    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix, 0);
     return p.grid > 0 && p.rw * p.kw == 4 && (p.rpw == 1 || p.rpw == 2);
 }
 
@@ -1522,7 +1534,7 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                               const int32_t* parent, int32_t* next_tokens, int32_t* accept_len,
                               int32_t* accepted_nodes, int32_t* bonus, void* accept_workspace,
                               int anc_from_parent, hipStream_t stream) {
-    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix, 0);
     AttnArgs a = make_attn_args(p, s, max_prefix, q, k_pages, v_pages, block_table, prefix_len, k_tree,
                                 v_tree, anc, out, lse, attn_workspace, nullptr, 0);
     const AcceptPlan ap = plan_accept(s.B, s.N, vocab);
@@ -1540,8 +1552,8 @@ hipError_t launch_verify_bf16(const jf_attn_shape& s, int max_prefix, const void
                       : launch_verify_d<64>(p, a, c, accept_grid, stream);
 }
 
-void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int32_t* out) {
-    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix);
+void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int ragged, int32_t* out) {
+    const AttnPlanBf16 p = plan_attention_bf16(s, max_prefix, ragged);
     out[0] = p.rb;
     out[1] = p.kw;
     out[2] = p.rpw;
@@ -1552,8 +1564,10 @@ void attention_bf16_plan(const jf_attn_shape& s, int max_prefix, int32_t* out) {
     out[7] = (int32_t)p.grid;
 }
 
+// Enough for the plan of jf_tree_attention and that of the ragged entry point.
 size_t attention_bf16_workspace_bytes(const jf_attn_shape& s, int max_prefix) {
-    return plan_attention_bf16(s, max_prefix).bytes;
+    const size_t a = plan_attention_bf16(s, max_prefix, 0).bytes, b = plan_attention_bf16(s, max_prefix, 1).bytes;
+    return a > b ? a : b;
 }
 
 }  // namespace jf
