@@ -3,9 +3,10 @@
 // exp. The table is filled with the C library's exp2, as the kernel fills it
 // with the device library's. exp_tab over its whole range: the largest error
 // in ulps of the result (normal results) and in subnormal steps (subnormal
-// results). exp_tab_nonpos over x <= 0: the largest relative error for
-// -40 <= x <= 0 and for -708 <= x < -40, and its special inputs (NaN, -inf and
-// x <= -746 give 0, zero gives exactly 1). Prints the figures and the points checked.
+// results). exp_tab_nonpos over x <= 0, with its own table (exp_tab_adjust): the
+// largest relative error for -40 <= x <= 0 and for -700 <= x < -40, and its special
+// inputs (NaN, -inf and x <= -700 give exp(-700), zero gives exactly 1). Prints
+// the figures and the points checked.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -19,8 +20,11 @@ static double ulp_of(double v) {
 }
 
 int main() {
-    double tab[256];
-    for (int j = 0; j < 256; ++j) tab[j] = std::exp2((double)j / 256.0);
+    double tab[256], tab_adj[256];
+    for (int j = 0; j < 256; ++j) {
+        tab[j] = std::exp2((double)j / 256.0);
+        tab_adj[j] = jf::exp_tab_adjust(tab[j], j);
+    }
     double max_ulp = 0.0, max_sub = 0.0, worst = 0.0;
     long points = 0;
     uint64_t state = 0x9e3779b97f4a7c15ull;   // splitmix64
@@ -37,13 +41,13 @@ int main() {
             if (!(x <= 0.0)) return;
             ++points;
             const double ref = std::exp(x);
-            const double got = jf::exp_tab_nonpos(x, tab);
-            if (x >= -708.0) {
+            const double got = jf::exp_tab_nonpos(x, tab_adj);
+            if (x >= -700.0) {
                 const double rel = std::fabs(got - ref) / ref;
                 double& slot = x >= -40.0 ? rel_near : rel_far;
                 if (rel > slot) slot = rel;
-            } else if (!(got <= 2.0 * ref + 1e-300)) {
-                rel_far = 1.0;                  // deep underflow: no more than twice the true value
+            } else if (!(std::fabs(got - std::exp(-700.0)) <= 1e-13 * std::exp(-700.0))) {
+                rel_far = 1.0;                  // below -700: exp(-700)
             }
             return;
         }
@@ -71,7 +75,7 @@ int main() {
     };
     // a dense grid over the whole range, every table slot at many offsets, and random
     // points; then the same points (those <= 0) for exp_tab_nonpos, with the special
-    // inputs it reads (NaN and -inf give 0, the clamp at -746, zero gives 1)
+    // inputs it reads (NaN and -inf give exp(-700), the clamp at -700, zero gives 1)
     for (int pass = 0; pass < 2; ++pass) {
         nonpos = pass == 1;
         for (long i = 0; i <= 4000000; ++i) check(-745.0 + (709.0 + 745.0) * (double)i / 4000000.0);
@@ -85,10 +89,10 @@ int main() {
         for (double x : {-745.5, -746.0, -746.5, -800.0, -1e300}) check(x);
     }
     long special_bad = 0;
-    for (double x : {(double)NAN, -(double)INFINITY, -746.0, -1e300})
-        special_bad += jf::exp_tab_nonpos(x, tab) != 0.0;
-    special_bad += jf::exp_tab_nonpos(0.0, tab) != 1.0;
-    special_bad += jf::exp_tab_nonpos(-0.0, tab) != 1.0;
+    for (double x : {(double)NAN, -(double)INFINITY, -700.0, -746.0, -1e300})
+        special_bad += !(std::fabs(jf::exp_tab_nonpos(x, tab_adj) - std::exp(-700.0)) <= 1e-13 * std::exp(-700.0));
+    special_bad += jf::exp_tab_nonpos(0.0, tab_adj) != 1.0;
+    special_bad += jf::exp_tab_nonpos(-0.0, tab_adj) != 1.0;
     for (long i = 0; i <= 4000000; ++i) {                   // exp_tab_nonpos where the scan's terms live
         nonpos = true;
         check(-40.0 * (double)i / 4000000.0);

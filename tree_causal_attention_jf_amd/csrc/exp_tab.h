@@ -31,12 +31,19 @@ __host__ __device__ inline double exp_tab(double x, const double* __restrict__ t
     return x > -745.2 ? e : 0.0;
 }
 
-// exp(x) for x <= 0, with a NaN read as -inf (result 0): the scan's terms
-// exp(z - m) against a reference m no smaller than any z, where each term only
-// has to be good to a relative 1e-13 (they are summed into a logsumexp whose
-// decisions need far less). Same table as exp_tab, three fused multiply-adds
-// fewer:
-//  * a max clamps x at -746 (and turns a NaN into -746);
+// Entry j of the table exp_tab_nonpos reads: 2^(j/256) with j << 44 taken from its
+// bit pattern (j << 12 from the high word), so that adding k << 12 to the high
+// word, where k & 255 == j, gives 2^(k >> 8) * 2^(j/256) exactly.
+__host__ __device__ inline double exp_tab_adjust(double t, int j) {
+    return __builtin_bit_cast(double, __builtin_bit_cast(unsigned long long, t) - ((unsigned long long)j << 44));
+}
+
+// exp(x) for x <= 0 (results down to exp(-700)): the scan's terms exp(z - m)
+// against a reference m no smaller than any z, where each term only has to be
+// good to a relative 1e-13 (they are summed into a logsumexp whose decisions need
+// far less). Same reduction as exp_tab, with these changes:
+//  * a max clamps x at -700 (and turns a NaN into -700): a NaN, -inf or x < -700
+//    gives exp(-700) ~ 1e-304, which vanishes beside the reference term, 1;
 //  * k = rint(x * 256/ln2) comes from one fused multiply-add with the rounding
 //    constant 1.5 * 2^52 (the sum's unit in the last place is 1, so k sits in the
 //    low word of its bit pattern, and k itself is the sum minus the constant);
@@ -46,22 +53,28 @@ __host__ __device__ inline double exp_tab(double x, const double* __restrict__ t
 //    |r| <= ln2/512 (relative error 2.4e-14; fitted as a linear program over a
 //    dense grid). It vanishes at r = 0, so exp(0) is exactly 1: a row with one
 //    finite logit gives that token a log-probability of exactly 0, and rows with
-//    equal maxima tie exactly.
+//    equal maxima tie exactly;
+//  * 2^(k >> 8) by an integer add to the table entry's high word (tab holds
+//    exp_tab_adjust(2^(j/256), j)): no ldexp, and at x >= -700 the exponent
+//    stays normal.
 // Measured relative error (tests/c_abi/exp_tab_check.cpp): at most 4e-14 for
-// -40 <= x <= 0, 1e-13 down to -708 (normal results). At -746 the result is 0.
+// -40 <= x <= 0, 1e-13 down to -700.
 __host__ __device__ inline double exp_tab_nonpos(double x, const double* __restrict__ tab) {
     constexpr double kInvStep = 369.3299304675746;           // 256 / ln 2
     constexpr double kStep = 0x1.62e42fefa39efp-9;           // ln 2 / 256
     constexpr double kShift = 0x1.8p52;
     constexpr double c1 = 0x1.00000000000d1p+0, c2 = 0x1.0000021f6e2c6p-1, c3 = 0x1.5555523a6aed1p-3;
-    const double xc = __builtin_fmax(x, -746.0);
+    const double xc = __builtin_fmax(x, -700.0);
     const double y = __builtin_fma(xc, kInvStep, kShift);
-    const int k = (int)(uint32_t)__builtin_bit_cast(unsigned long long, y);
+    const unsigned k = (unsigned)__builtin_bit_cast(unsigned long long, y);
     const double kd = y - kShift;
     const double r = __builtin_fma(-kd, kStep, xc);
     const double p = r * __builtin_fma(r, __builtin_fma(r, c3, c2), c1);
-    const double t = tab[k & 255];
-    return __builtin_ldexp(__builtin_fma(t, p, t), k >> 8);
+    typedef unsigned words2 __attribute__((ext_vector_type(2)));   // (low word, high word)
+    words2 tw = __builtin_bit_cast(words2, tab[k & 255]);
+    tw.y += k << 12;                                               // one 32-bit add on the high word
+    const double t = __builtin_bit_cast(double, tw);
+    return __builtin_fma(t, p, t);
 }
 
 }  // namespace jf

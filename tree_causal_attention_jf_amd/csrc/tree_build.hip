@@ -644,7 +644,7 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ float s_m[kNW], s_tau[kNW];
     __shared__ double s_s[kNW];
     __shared__ int s_last;
-    __shared__ double s_exp2[256];                            // 2^(j/256) for exp_tab
+    __shared__ double s_exp2[256];                            // 2^(j/256), adjusted for exp_tab_nonpos
     // growth in batches: grown nodes' scores, depths, next child ranks; candidates
     __shared__ double s_nsc[JF_MAX_NODES];
     __shared__ int s_dep[JF_MAX_NODES], s_r[JF_MAX_NODES];
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
     }
     if (i >= rows_live) return;
     static_assert(kBuildThreads >= 256, "one table entry per thread");
-    if (t < 256) s_exp2[t] = exp2((double)t / 256.0);
+    if (t < 256) s_exp2[t] = exp_tab_adjust(exp2((double)t / 256.0), t);   // the table exp_tab_nonpos reads
     __syncthreads();
 
     // ---- phase 1: one chunk of row i, kBuildVecs 16-byte vectors per thread, all
