@@ -1,4 +1,4 @@
-// exp(x) in fp64 from a 256-entry table of 2^(j/256), for the tree
+// exp(x) in fp64 for x <= 0 from a 256-entry table of 2^(j/256), for the tree
 // construction kernel's per-value exponentials. Host and device: the same
 // source is checked against the C library's exp on the CPU
 // (tests/c_abi/exp_tab_check.cpp).
@@ -8,28 +8,6 @@
 #include <cstdint>
 
 namespace jf {
-
-// exp(x) for x <= 709 (0 below -745.2). x = k ln2/256 + r with k integer
-// (Cody-Waite: ln2/256 split into a 31-bit head, so k * head is exact for
-// |k| < 2^22, and a tail), |r| <= ln2/512; e^r = 1 + p(r) with p the degree-4
-// Taylor polynomial (remainder r^5/120 < 4e-17); e^x = 2^(k>>8) * tab[k&255] * e^r
-// with tab[j] = 2^(j/256). Measured error, with the table from the C library's
-// exp2: at most 1 ulp against the C library's exp over [-745, 709] (normal
-// results; subnormal results within one subnormal step). Four fused
-// multiply-adds instead of the dozen of a general-purpose exp.
-__host__ __device__ inline double exp_tab(double x, const double* __restrict__ tab) {
-    constexpr double kInvStep = 369.3299304675746;          // 256 / ln 2
-    constexpr double kStepHi = 0x1.62e42fec00000p-9;         // ln 2 / 256, leading 31 bits
-    constexpr double kStepLo = 0x1.d1cf79abc9e3bp-40;        // ln 2 / 256 - kStepHi
-    const double xc = x > -746.0 ? x : -746.0;
-    const double kd = __builtin_rint(xc * kInvStep);
-    const int k = (int)kd;
-    const double r = __builtin_fma(-kd, kStepLo, __builtin_fma(-kd, kStepHi, xc));
-    const double p = r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0))));
-    const double t = tab[k & 255];
-    const double e = __builtin_ldexp(__builtin_fma(t, p, t), k >> 8);
-    return x > -745.2 ? e : 0.0;
-}
 
 // Entry j of the table exp_tab_nonpos reads: 2^(j/256) with j << 44 taken from its
 // bit pattern (j << 12 from the high word), so that adding k << 12 to the high
@@ -41,7 +19,8 @@ __host__ __device__ inline double exp_tab_adjust(double t, int j) {
 // exp(x) for x <= 0 (results down to exp(-700)): the scan's terms exp(z - m)
 // against a reference m no smaller than any z, where each term only has to be
 // good to a relative 1e-13 (they are summed into a logsumexp whose decisions need
-// far less). Same reduction as exp_tab, with these changes:
+// far less). x = k ln2/256 + r with k an integer and |r| <= ln2/512, and
+// e^x = 2^(k >> 8) * tab[k & 255] * e^r with tab[j] = 2^(j/256):
 //  * a max clamps x at -700 (and turns a NaN into -700): a NaN, -inf or x < -700
 //    gives exp(-700) ~ 1e-304, which vanishes beside the reference term, 1;
 //  * k = rint(x * 256/ln2) comes from one fused multiply-add with the rounding
