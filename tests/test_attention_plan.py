@@ -50,7 +50,8 @@ def test_one_sequence_grid_never_exceeds_the_cus(jf):
                                          (1, 4, 8), (1, 4, 8)):
         p = plan(jf, L, N=N, Hkv=Hkv, Hq=Hkv * G)
         # unless a split's page list (at most 1024 pages) forces more splits
-        assert p["workgroups"] <= 256 or p["pages_per_split"] == 1024, (L, N, Hkv, G, p)
+        pages = (L + 15) // 16
+        assert p["workgroups"] <= 256 or p["splits"] == (pages + 1023) // 1024, (L, N, Hkv, G, p)
         assert p["splits"] >= 1 and p["pages_per_split"] % 4 == 0
 
 
@@ -59,6 +60,16 @@ def test_one_sequence_few_items_take_128_row_blocks(jf):
     # 128-row blocks with two key groups give 64 items x 4 splits
     p = plan(jf, 8192, N=256)
     assert (p["rows_per_workgroup"], p["key_groups"], p["splits"], p["workgroups"]) == (128, 2, 4, 256)
+    # the 4 tree tiles count as 16 pages when the splits are sized: (512 + 16) / 4 = 132 pages
+    # per split, so the last split holds 116 prefix pages plus the tree (33 tiles each)
+    assert p["pages_per_split"] == 132 and p["tree_split"] == 0
+
+
+def test_tree_pages_never_change_the_split_count(jf):
+    for L, N in itertools.product((700, 2048, 4096, 8192, 8200, 32768), (64, 128, 256)):
+        p = plan(jf, L, N=N)
+        pages = (L + 15) // 16
+        assert (pages + p["pages_per_split"] - 1) // p["pages_per_split"] == p["splits"] - p["tree_split"], (L, N, p)
 
 
 def test_one_sequence_256_row_blocks_leave_cus_free(jf):

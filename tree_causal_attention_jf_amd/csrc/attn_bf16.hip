@@ -1387,6 +1387,19 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix, int rag
         p.splits = splits;
         p.grid = (long)p.items * splits;
     }
+    // one sequence whose tree tiles ride on the last prefix split: count them as pages
+    // when sizing the splits, so the last split takes that many fewer prefix pages and
+    // no split runs longer than the others (draft head's pass, 1 x 256 nodes over 8192:
+    // 32 + 4 tree tiles on the last of four splits -> 33 tiles on each)
+    if (!p.balanced && !p.tree_split && splits > 1 && env_int("JF_TREE_PAGES", 1)) {
+        const int tree_pages = 4 * ((s.N + kKeyTile - 1) / kKeyTile);
+        int even = (max_pages + tree_pages + splits - 1) / splits;
+        even = (even + 3) / 4 * 4;
+        if (even <= kMaxPagesPerSplit && (max_pages + even - 1) / even == splits) {
+            pps = even;
+            p.pps = pps;
+        }
+    }
     if (splits > 1) {
         // counters: the fixed region of every workspace (self-cleaning), extended past
         // it, and zero-filled before the launch, only for more than kMaxCounters items
