@@ -282,6 +282,31 @@ def test_attention_bf16_balanced_skewed(jf, lens):
         check_bf16(out, ref, lse, lref, f"lens {lens} D {D}", abs_tol=derived_bf16_bar(wl))
 
 
+@pytest.mark.parametrize("ht", ["1.1", "0"])
+@pytest.mark.parametrize("cus,lens,shape", [
+    # four row blocks per (sequence, KV head): three sequences cut (heads of 49 tiles), five whole
+    (64, [3904, 3840, 3584, 1344, 1024, 1664, 2304, 2944],
+     dict(N=256, Hq=8, Hkv=2, D=128, tree=("best_first", 4, 12, 2.0))),
+    # d = 64, one row block per (sequence, KV head): two sequences cut
+    (72, [2000, 1500, 1900, 1000, 1300, 1100, 600, 1800], dict(N=80, Hq=16, Hkv=8, D=64, tree=("random", 7))),
+], ids=["d128_cut3", "d64_cut2"])
+def test_attention_bf16_head_and_tail(jf, cus, lens, shape, ht, monkeypatch):
+    # A batch in 256-row blocks whose equal pieces fill the CUs in one round
+    # (JF_TARGET_WG sets the CU count the plan divides the work by) takes the
+    # head-and-tail rule in the kernel's balanced schedule: a long sequence keeps
+    # a head of 1.1x the mean work per CU and hands the rest, with its tree tiles,
+    # to a tail piece that starts on a CU a short sequence has freed. JF_BAL_HT=0
+    # keeps equal pieces. Every piece layout must give the oracle's result.
+    monkeypatch.setenv("JF_TARGET_WG", str(cus))
+    monkeypatch.setenv("JF_BAL_HT", ht)
+    wl = W.make_workload("c1_chain16", 23, with_accept=False, B=len(lens), prefix=("list", lens), **shape)
+    assert jf.tree_attention_plan(jf.attn_shape(wl.q, wl.k_pages, wl.block_table, wl.sm_scale),
+                                  wl.max_prefix_len)["balanced"] == 1
+    out, lse = run_attention(jf, wl, to_dev(wl))
+    ref, lref = _oracle_full(wl)
+    check_bf16(out, ref, lse, lref, f"cus {cus} lens {lens} ht {ht}", abs_tol=derived_bf16_bar(wl))
+
+
 def test_one_workspace_serves_every_shape(jf, monkeypatch):
     # one workspace, used in turn by attention calls whose partial layouts differ
     # and by logits-mode acceptance: each call must find the counter region zero

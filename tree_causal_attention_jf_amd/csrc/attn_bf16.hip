@@ -67,6 +67,7 @@ constexpr int kMaxPagesPerSplit = 1024;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxTreePages = JF_MAX_NODES / 16 + 1;   // pages a paged tree of up to 256 nodes spans
 constexpr int kMaxBalanced = 64;         // batches planned from their prefix lengths inside the kernel (one wave)
+constexpr int kMinTail = 8;              // balanced: smallest tail piece (tiles) of the head-and-tail rule
 
 struct AttnArgs {
     const uint16_t* q;
@@ -95,6 +96,7 @@ struct AttnArgs {
     int cus;           // compute units of the device (ditto)
     int forced;        // balanced: every sequence takes `splits` pieces (tuning and tests)
     float cut;         // balanced: a sequence is cut when its work exceeds cut x the mean per CU
+    float ht_frac;     // balanced: head size of the head-and-tail rule, x the mean per CU (0: off)
     const int32_t* tree_len;  // [B] nodes of each tree (NULL: all N); rows of later nodes are not written
     int paged_tree;    // 1: node j's K/V is cached token prefix_len[b] + j (kt / vt unused)
     int tree_split;    // 1: split splits-1 runs the tree tiles alone, the others the prefix
@@ -576,24 +578,33 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     int rb, s, kvh, b, pps;
     if (a.balanced) {
         // Balanced schedule, planned alike by every workgroup from the prefix (and
-        // tree) lengths:
-        //  * a sequence whose work per workgroup (prefix tiles + tree tiles) exceeds
-        //    1.5x the mean work per CU is cut into ceil(work / mean) pieces (at most
-        //    `splits`) of equal page counts; the mean counts only row blocks that
-        //    hold rows of the tree (the others exit at once);
-        //  * units (sequence, piece, KV head) are ranked by piece size, largest first,
-        //    and dealt round robin to the XCDs; a unit's nrb row blocks (which read
-        //    the same K/V pages) run one after another on one XCD.
-        // Each XCD starts its workgroups in id order as its CUs free up, so it
-        // list-schedules its own longest-first share. Ids past the units are idle.
+        // tree) lengths. The mean is the work per CU (prefix tiles + tree tiles, over
+        // the row blocks that hold rows of the tree; the others exit at once). Two
+        // rules cut sequences into pieces:
+        //  * equal pieces: a sequence whose work exceeds `cut` x the mean is cut into
+        //    ceil(work / mean) pieces (at most `splits`) of equal page counts;
+        //  * head and tail, used instead when the equal pieces fit the CUs in one round
+        //    (so nothing else would take over the CUs the short sequences free) and
+        //    the tails do not: a sequence at least kMinTail tiles above ht_frac x the
+        //    mean keeps a head of that many prefix tiles (at least half its pages)
+        //    and hands the rest, with its tree tiles, to a tail piece. Tails rank low,
+        //    so they start on the CUs that the short sequences free first, and end
+        //    beside the heads instead of after them.
+        // Units (sequence, piece, KV head) are ranked by piece size, largest first,
+        // and dealt round robin to the XCDs; a unit's nrb row blocks (which read the
+        // same K/V pages) run one after another on one XCD. Each XCD starts its
+        // workgroups in id order as its CUs free up, so it list-schedules its own
+        // longest-first share. Ids past the units are idle.
         if (w == 0) {
-            const int Lm = lane < a.B ? a.prefix_len[lane] : 0;
-            int nbm = (a.tree_len && lane < a.B) ? a.tree_len[lane] : a.N;
+            const bool in = lane < a.B;
+            const int Lm = in ? a.prefix_len[lane] : 0;
+            int nbm = (a.tree_len && in) ? a.tree_len[lane] : a.N;
             if (nbm < 0 || nbm > a.N) nbm = a.N;       // a bad length computes every row (as NaN)
-            const int pg = (lane < a.B && Lm > 0 && Lm <= a.max_prefix) ? (Lm + kPage - 1) / kPage : 0;
-            const int tiles = (pg + 3) / 4 + min(a.tree_tiles, (nbm + kKeyTile - 1) / kKeyTile);
+            const int pg = (in && Lm > 0 && Lm <= a.max_prefix) ? (Lm + kPage - 1) / kPage : 0;
+            const int ttl = min(a.tree_tiles, (nbm + kKeyTile - 1) / kKeyTile);
+            const int tiles = (pg + 3) / 4 + ttl;
             const int live = min(a.nrb, (nbm * a.G + RB - 1) / RB);        // row blocks with rows
-            int tot = lane < a.B ? tiles * live : 0;
+            int tot = in ? tiles * live : 0;
             #pragma unroll
             for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
             const float mean = (float)tot * (float)a.Hkv / (float)a.cus;
@@ -605,24 +616,71 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
             n = max(n, (pg + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit);  // (the host keeps this <= splits)
             int pp = (pg + n - 1) / n;
             pp = max(4, (pp + 3) / 4 * 4);
-            n = lane < a.B ? max(1, (pg + pp - 1) / pp) : 0;
-            const int key = lane < a.B ? min(pp, pg) : -1;
-            int off = 0;                               // units of the sequences ranked before this one
-            for (int j = 0; j < a.B; ++j) {
-                const int kj = __shfl(key, j), nj = __shfl(n, j);
-                off += (kj > key || (kj == key && j < lane)) ? nj : 0;
+            n = in ? max(1, (pg + pp - 1) / pp) : 0;
+            // head and tail: head pages h, a multiple of 4 and at least half the prefix,
+            // so that the two pieces [0, h) and [h, pg) are the splits of h pages each
+            const int T = (int)(a.ht_frac * mean + 0.5f);
+            const int h = max(4 * T, (pg + 7) / 8 * 4);
+            const bool cut2 = in && !a.forced && a.ht_frac > 0.f && live > 0 && tiles - T >= kMinTail &&
+                              h < pg && h >= 4 * KW && h <= kMaxPagesPerSplit;
+            int wgs = in ? (cut2 ? 2 : 1) * live * a.Hkv : 0;     // workgroups with head and tail pieces
+            int wgs_eq = in ? n * live * a.Hkv : 0;                // with equal pieces
+            int big = pg > kMaxPagesPerSplit;                      // must be cut however long the others are
+            #pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                wgs += __shfl_xor(wgs, o);
+                wgs_eq += __shfl_xor(wgs_eq, o);
+                big |= __shfl_xor(big, o);
+            }
+            // (256-row blocks only: the 128-row plans measured slower with it)
+            const bool ht = KW == 1 && a.ht_frac > 0.f && !a.forced && !big && wgs_eq <= a.cus && wgs > a.cus;
+            // a sequence's pieces in two groups of equal keys (pieces of one group are
+            // consecutive in the ranking): na pieces of key ka, then nb of key kb
+            int na = n, ka = in ? min(pp, pg) : -1, nb = 0, kb = -1;
+            if (ht && in) {
+                na = 1;
+                if (cut2) {
+                    pp = h;
+                    ka = h;
+                    nb = 1;
+                    kb = (pg - h) + 4 * ttl;
+                } else {
+                    pp = max(4, (pg + 3) / 4 * 4);
+                    ka = pg + 4 * ttl;
+                }
+            }
+            // units ranked before each group: larger keys first, ties by sequence,
+            // then group (without tails, one group per sequence: the shorter loop)
+            int offa = 0, offb = 0;
+            if (ht) {
+                const int nab = na | (nb << 16);
+                for (int j = 0; j < a.B; ++j) {
+                    const int kaj = __shfl(ka, j), kbj = __shfl(kb, j), nabj = __shfl(nab, j);
+                    const int naj = nabj & 0xffff, nbj = nabj >> 16;
+                    offa += ((kaj > ka || (kaj == ka && j < lane)) ? naj : 0) +
+                            ((kbj > ka || (kbj == ka && j < lane)) ? nbj : 0);
+                    offb += ((kaj > kb || (kaj == kb && j <= lane)) ? naj : 0) +
+                            ((kbj > kb || (kbj == kb && j < lane)) ? nbj : 0);
+                }
+            } else {
+                for (int j = 0; j < a.B; ++j) {
+                    const int kaj = __shfl(ka, j), naj = __shfl(na, j);
+                    offa += (kaj > ka || (kaj == ka && j < lane)) ? naj : 0;
+                }
             }
             const int slot = bid / kNumXcd;
             const int u = (slot / a.nrb) * kNumXcd + bid % kNumXcd;
-            const int lo = off * a.Hkv;
-            const bool mine = lane < a.B && u >= lo && u < lo + n * a.Hkv;
-            if (mine) {
+            const int loa = offa * a.Hkv, lob = offb * a.Hkv;
+            const bool mine_a = in && u >= loa && u < loa + na * a.Hkv;
+            const bool mine_b = in && nb > 0 && u >= lob && u < lob + nb * a.Hkv;
+            if (mine_a || mine_b) {
+                const int lo = mine_a ? loa : lob;
                 s_plan[0] = lane;
-                s_plan[1] = (u - lo) / a.Hkv;
+                s_plan[1] = (mine_a ? 0 : na) + (u - lo) / a.Hkv;
                 s_plan[2] = (u - lo) % a.Hkv;
                 s_plan[3] = pp;
             }
-            if (__ballot(mine) == 0 && lane == 0) s_plan[0] = -1;
+            if (__ballot(mine_a || mine_b) == 0 && lane == 0) s_plan[0] = -1;
         }
         __syncthreads();
         b = __builtin_amdgcn_readfirstlane(s_plan[0]);
@@ -1471,6 +1529,8 @@ static AttnArgs make_attn_args(const AttnPlanBf16& p, const jf_attn_shape& s, in
     {
         const char* v = getenv("JF_BAL_CUT");
         a.cut = (v && *v) ? (float)atof(v) : 1.5f;
+        const char* f = getenv("JF_BAL_HT");
+        a.ht_frac = (f && *f) ? (float)atof(f) : 1.1f;
     }
     a.tree_split = p.tree_split;
     a.tree_len = tree_len;
