@@ -451,6 +451,22 @@ def test_attention_deterministic(jf):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("rw", [8, 4])
+def test_attention_deterministic_many_splits(jf, rw, monkeypatch):
+    # eight splits per item, merged by whichever split arrives last: the merged
+    # output must not depend on that order (the last arriver merges its own
+    # partial as stored, in split order), with and without key groups
+    monkeypatch.setenv("JF_RW", str(rw))
+    monkeypatch.setenv("JF_SPLITS", "8")
+    monkeypatch.setenv("JF_BALANCED", "0")
+    wl = W.make_workload("c2_bf256_b8", 4, with_accept=False, B=2)
+    d = to_dev(wl)
+    o1, l1 = run_attention(jf, wl, d)
+    for _ in range(4):
+        o2, l2 = run_attention(jf, wl, d)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 def test_attention_mask_leak_exact(jf):
     # randomising K/V of nodes outside a row's path leaves that row bit-identical
     wl = W.make_workload("c1_chain16", 5, with_accept=False, B=1, N=64, prefix=("fixed", 90), Hq=4, Hkv=1,

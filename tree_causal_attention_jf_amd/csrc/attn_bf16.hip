@@ -83,8 +83,8 @@ struct AttnArgs {
     float* lse;
     int* counters;     // [items]                       zero between calls
     float* part_ml;    // [items][splits][RB][4]        (m in log2 units, l, row scale r, unused)
-    float* part_o;     // [items][splits] x [RB][D]     unnormalised: fp32 fragment-major (part_off) with one
-                       //                               key group, else fp16 of O / r (half_off)
+    float* part_o;     // [items][splits] x [RB][D]     fp16 of O / r: in the MFMA layout (frag_half_off)
+                       //                               with one key group, else row-major (half_off)
     uint32_t part_ml_bytes, part_o_bytes;
     int B, N, Hq, Hkv, G, num_pages, max_pages, max_prefix;
     int rows;          // G * N
@@ -483,20 +483,16 @@ __device__ __forceinline__ int merge_off(int r, int c) {
     return r * (D * 4) + ((c ^ (r & 7)) << 4);
 }
 
-// Float offset of float4 chunk c (columns 4c..4c+3) of row r within one split's
-// [RB][D] partial O, in one of two layouts, each chosen so that every store
-// instruction of its producer writes whole 128-byte lines (the hand-off stores
-// write through to memory, where partial lines cost extra transactions):
-//  - fragment-major (FRAG, for the tile loop's own MFMA layout): per 32-row block
-//    and output fragment (dt, rq), 64 lanes x 16 B = 1 KB, lane = (r % 32) + 32 (c % 2);
-//  - row-major (after the key-group merge, whose threads own chunks part, part + TPR, ...).
-template <int D, bool FRAG>
-__device__ __forceinline__ uint32_t part_off(int r, int c) {
-    constexpr int DT = D / 32;
-    if constexpr (FRAG)
-        return (uint32_t)(((((r >> 5) * DT + (c >> 3)) * 4 + ((c >> 1) & 3)) * 64 + (r & 31) + 32 * (c & 1)) * 4);
-    else
-        return (uint32_t)(r * D + c * 4);
+// Byte offset, inside one split's [RB][D] fp16 partial, of the k-th 16 bytes
+// that a lane of the tile loop's MFMA layout holds (one key group: lane = row
+// r % 32 + 32 hf of its 32-row block, holding the row's chunks 2j + hf, j = 0 ..
+// D/8 - 1; store k packs chunks 4k + hf and 4k + 2 + hf). One store instruction
+// writes one contiguous 1 KB block (the hand-off stores write through to
+// memory, where partial lines cost extra transactions), and the last arriver,
+// which merges in the same layout, reads it back the same way.
+template <int D>
+__device__ __forceinline__ uint32_t frag_half_off(int r, int hf, int k) {
+    return (uint32_t)((((r >> 5) * (D / 16) + k) * 64 + (r & 31) + 32 * hf) * 16);
 }
 
 // Byte offset, inside one split's [RB][D] fp16 partial, of the 16 bytes that
@@ -547,10 +543,10 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
 template <int D, int RW, int KW, int RPW>
 __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const unsigned bid, const unsigned nblk) {
     using Gm = Geo<D>;
-    constexpr bool kFragPart = KW == 1;              // split partial layout (part_off)
-    // With key groups the merged partial is written as fp16 of O / r, r the row's
-    // largest |O| (values in [-1, 1]: no overflow, 2^-11 of r per value), half the
-    // bytes of fp32 for the last arriver to read
+    // Split partials are written as fp16 of O / r, r the row's largest |O| (values
+    // in [-1, 1]: no overflow, 2^-11 of r per value), half the bytes of fp32 for
+    // the last arriver to read: after the key-group merge in row-major order
+    // (half_off), without key groups in the MFMA layout (frag_half_off)
     constexpr bool kHalfPart = KW > 1;
     constexpr int NW = RW * KW;
     constexpr int T = NW * 64;
@@ -1005,6 +1001,10 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     float* mo = reinterpret_cast<float*>(ring);      // key-group merge area (reuses the ring)
 
     // ---- one row block's result, as (m, l, unnormalised O) per row
+    // (one key group: the split's fp16 partial as stored, and its m, l and row
+    // scale, kept for the merge if this workgroup arrives last)
+    u32x4 hp[RPW][D / 16];
+    float own_m[RPW], own_l[RPW], own_r[RPW];
     if constexpr (KW == 1) {
         #pragma unroll
         for (int blk = 0; blk < RPW; ++blk) {
@@ -1035,18 +1035,31 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
             const uint32_t psplit = ((uint32_t)item * a.splits + s) * RB;
             const uint32_t pr = psplit + rloc[blk];
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
+            // the row's scale: its largest |O| over both half-waves' 64 values each
+            float r = 0.f;
             #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const f32x4 v = {sb.o[dt][4 * rq], sb.o[dt][4 * rq + 1], sb.o[dt][4 * rq + 2], sb.o[dt][4 * rq + 3]};
-                    st16(ro, (psplit * D + part_off<D, kFragPart>(rloc[blk], dt * 8 + 2 * rq + h2f)) * 4, v);
-                }
+                for (int i = 0; i < 16; ++i) r = fmaxf(r, fabsf(sb.o[dt][i]));
             }
-            if (h2f == 0) {
-                const u32x2 ml = {__float_as_uint(bad ? NANF : sb.m), __float_as_uint(bad ? NANF : l_tot)};
-                st8(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 16, ml);
+            r = fmaxf(r, __shfl_xor(r, 32));
+            const float rinv = r > 0.f ? 1.f / r : 0.f;
+            // store k: chunks j = 2k and 2k + 1 of the lane (O registers dt = j / 4,
+            // 4 (j % 4) .. 4 (j % 4) + 3)
+            #pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                const int d0 = (2 * k) >> 2, q0 = 4 * ((2 * k) & 3), d1 = (2 * k + 1) >> 2, q1 = 4 * ((2 * k + 1) & 3);
+                hp[blk][k] = u32x4{pack_f16x2(sb.o[d0][q0] * rinv, sb.o[d0][q0 + 1] * rinv),
+                                   pack_f16x2(sb.o[d0][q0 + 2] * rinv, sb.o[d0][q0 + 3] * rinv),
+                                   pack_f16x2(sb.o[d1][q1] * rinv, sb.o[d1][q1 + 1] * rinv),
+                                   pack_f16x2(sb.o[d1][q1 + 2] * rinv, sb.o[d1][q1 + 3] * rinv)};
+                st16(ro, psplit * (D * 2) + frag_half_off<D>(rloc[blk], h2f, k), __builtin_bit_cast(f32x4, hp[blk][k]));
             }
+            own_m[blk] = bad ? NANF : sb.m;
+            own_l[blk] = bad ? NANF : l_tot;
+            own_r[blk] = r;
+            if (h2f == 0)
+                st16(make_rsrc(a.part_ml, a.part_ml_bytes), pr * 16, f32x4{own_m[blk], own_l[blk], r, 0.f});
         }
         if (n_act == 1) return;
     } else {
@@ -1225,78 +1238,85 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                 a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
         }
         } else {
-        constexpr int TPR = T / RB;                // threads per row
-        constexpr int CPT = D / 4 / TPR;           // float4 chunks per thread
-        constexpr int CB = CPT < 16 ? CPT : 16;    // chunks per pass over the splits
-        // splits per batch: up to 32 float4 in flight per thread, 64 in the four-wave
-        // layouts (one wave per SIMD: twice the registers)
-        constexpr int INFLIGHT = NW <= 4 ? 64 : 32;
-        constexpr int SB = (INFLIGHT / CB) > 1 ? (INFLIGHT / CB) : 1;
-        const int rl = tid / TPR, part = tid % TPR;
-        const int grow = rb * RB + rl;
+        // One key group: every lane merges its own row's chunks in the tile loop's
+        // layout, as the splits stored them. This workgroup's own partial comes from
+        // registers (the fp16 values it stored, so the result does not depend on
+        // which split arrives last); the others' are loaded, every split's loads of a
+        // batch at once.
+        constexpr int NK = D / 16;                 // 16-byte pieces of a lane's partial
+        constexpr int SB = 32 / (NK + 1) > 1 ? 32 / (NK + 1) : 1;    // splits per batch
+        const int own_kk = (a.tree_split && s == a.splits - 1) ? n_pre_e : s;
         const uint32_t base = (uint32_t)item * a.splits * RB;        // + slot * RB
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, a.part_o_bytes);
         const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, a.part_ml_bytes);
-        const bool out_ok = grow < a.rows && grow / a.G < nb_e;
-        const int gnode = out_ok ? grow / a.G : 0, ghead = kvh * a.G + (out_ok ? grow % a.G : 0);
-        // the thread's CPT chunks in passes of CB; per pass, one batch of loads (every
-        // split's m, l and O slice) per SB splits, merged with a running max so no
-        // batch waits for another
-        for (int c0 = 0; c0 < CPT; c0 += CB) {
+        #pragma unroll
+        for (int blk = 0; blk < RPW; ++blk) {
             float M = NEG;
-            f32x4 acc[CB];
+            f32x4 acc[D / 8];
             #pragma unroll
-            for (int c = 0; c < CB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < D / 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
             float Ls = 0.f;
             for (int sp0 = 0; sp0 < n_act; sp0 += SB) {
-                f32x4 v[SB][CB];
-                u32x2 ml[SB];
+                u32x4 v[SB][NK];
+                f32x4 ml[SB];
                 #pragma unroll
                 for (int j = 0; j < SB; ++j) {
                     const int kk = sp0 + j;
-                    if (kk < n_act) {                  // uniform: slots past the last split load nothing
+                    if (kk == own_kk) {                // uniform
+                        #pragma unroll
+                        for (int k = 0; k < NK; ++k) v[j][k] = hp[blk][k];
+                        ml[j] = f32x4{own_m[blk], own_l[blk], own_r[blk], 0.f};
+                    } else if (kk < n_act) {           // uniform: slots past the last split load nothing
                         const int slot = (a.tree_split && kk >= n_pre_e) ? a.splits - 1 : kk;
                         const uint32_t ps = base + (uint32_t)slot * RB;
                         #pragma unroll
-                        for (int c = 0; c < CB; ++c)
-                            v[j][c] = ld16(ro, (ps * D + part_off<D, kFragPart>(rl, (c0 + c) * TPR + part)) * 4);
-                        ml[j] = ld8(rml, (ps + rl) * 16);
+                        for (int k = 0; k < NK; ++k)
+                            v[j][k] = __builtin_bit_cast(u32x4, ld16(ro, ps * (D * 2) + frag_half_off<D>(rloc[blk], hf, k)));
+                        ml[j] = ld16(rml, (ps + rloc[blk]) * 16);
                     } else {
                         #pragma unroll
-                        for (int c = 0; c < CB; ++c) v[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        ml[j] = u32x2{__float_as_uint(NEG), 0u};
+                        for (int k = 0; k < NK; ++k) v[j][k] = u32x4{0u, 0u, 0u, 0u};
+                        ml[j] = f32x4{NEG, 0.f, 0.f, 0.f};
                     }
                 }
                 float mb = NEG;
                 #pragma unroll
-                for (int j = 0; j < SB; ++j) mb = fmaxf(mb, __uint_as_float(ml[j][0]));
+                for (int j = 0; j < SB; ++j) mb = fmaxf(mb, ml[j][0]);
                 const float Mn = fmaxf(M, mb);
                 const float Mn_use = (Mn == NEG) ? 0.f : Mn;
                 const float sc = __builtin_amdgcn_exp2f(M - Mn_use);                      // M = -inf -> 0
                 Ls *= sc;
                 #pragma unroll
-                for (int c = 0; c < CB; ++c) acc[c] *= sc;
+                for (int c = 0; c < D / 8; ++c) acc[c] *= sc;
                 #pragma unroll
                 for (int j = 0; j < SB; ++j) {
-                    const float wgt =
-                        (sp0 + j < n_act) ? __builtin_amdgcn_exp2f(__uint_as_float(ml[j][0]) - Mn_use) : 0.f;
-                    Ls += wgt * __uint_as_float(ml[j][1]);
-                    #pragma unroll
-                    for (int c = 0; c < CB; ++c) acc[c] += wgt * v[j][c];
+                    if (sp0 + j < n_act) {             // uniform: no work for slots past the last split
+                        const float wgt = __builtin_amdgcn_exp2f(ml[j][0] - Mn_use);
+                        Ls += wgt * ml[j][1];
+                        const float wr = wgt * ml[j][2];                                  // weight x row scale
+                        #pragma unroll
+                        for (int k = 0; k < NK; ++k) {
+                            acc[2 * k] += wr * unpack_f16x4(v[j][k][0], v[j][k][1]);
+                            acc[2 * k + 1] += wr * unpack_f16x4(v[j][k][2], v[j][k][3]);
+                        }
+                    }
                 }
                 M = Mn;
             }
-            if (out_ok) {
+            if (row_ok[blk]) {
+                // opaque copies, as for the direct store above
+                int nd = node[blk], hd = head[blk], h2f = hf;
+                asm volatile("" : "+v"(nd), "+v"(hd), "+v"(h2f));
                 const float inv = 1.f / Ls;
-                uint16_t* op = a.out + (((long)b * a.N + gnode) * a.Hq + ghead) * D + (c0 * TPR + part) * 4;
+                uint16_t* op = a.out + (((long)b * a.N + nd) * a.Hq + hd) * D + 4 * h2f;
                 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    const u32x2 v = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
+                for (int c = 0; c < D / 8; ++c) {               // acc[c]: d = 8c + 4 hf .. + 3
+                    const u32x2 o = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv),
                                      pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + 4 * TPR * c) = v;
+                    *reinterpret_cast<u32x2*>(op + 8 * c) = o;
                 }
-                if (a.lse && part == 0 && c0 == 0)
-                    a.lse[((long)b * a.N + gnode) * a.Hq + ghead] = (M + __log2f(Ls)) * LN2;
+                if (a.lse && h2f == 0)
+                    a.lse[((long)b * a.N + nd) * a.Hq + hd] = (M + __log2f(Ls)) * LN2;
             }
         }
         }
@@ -1465,8 +1485,8 @@ AttnPlanBf16 plan_attention_bf16(const jf_attn_shape& s, int max_prefix, int rag
         p.fill_bytes = p.items > kMaxCounters ? align256((size_t)(p.items - kMaxCounters) * 4) : 0;
         p.off_ml = kCounterBytes + p.fill_bytes;
         p.off_o = p.off_ml + align256((size_t)p.items * splits * p.rb * 4 * 4);
-        // fp16 partials with key groups (four-wave plans), fp32 without
-        p.bytes = p.off_o + align256((size_t)p.items * splits * p.rb * s.D * (p.kw > 1 ? 2 : 4));
+        // fp16 partials: O / r with r the row's largest |O|
+        p.bytes = p.off_o + align256((size_t)p.items * splits * p.rb * s.D * 2);
     }
     return p;
 }
