@@ -100,6 +100,23 @@ def test_paged_tree_row_blocks_past_the_budget(jf, balanced, monkeypatch):
     _check(case, out, lse, what=f"balanced {balanced}")
 
 
+@pytest.mark.parametrize("rw,cus", [(4, 256), (4, 24), (8, 256), (8, 40)])
+def test_paged_tree_live_row_blocks_only(jf, rw, cus, monkeypatch):
+    # the balanced schedule gives workgroups to the row blocks that hold rows of a
+    # tree only, packed per XCD in rank order; with few CUs (JF_TARGET_WG) each XCD
+    # holds several units one after another, and in 256-row blocks long sequences
+    # may be cut into head and tail. Budgets 0, 1, 3 and full beside ragged ones.
+    monkeypatch.setenv("JF_RW", str(rw))
+    monkeypatch.setenv("JF_TARGET_WG", str(cus))
+    lens = [900, 40, 2000, 300, 17, 1500, 640, 1100, 64, 2600]
+    budgets = [256, 3, 130, 0, 70, 1, 200, 47, 256, 90]
+    case = W.make_paged_tree_case(37, lens, budgets, N=256, Hq=8, Hkv=2, D=128, tree=("best_first", 4, 12, 2.0))
+    assert jf.tree_attention_plan(jf.attn_shape(case.q, case.k_pages, case.block_table, case.sm_scale),
+                                  case.max_prefix_len, paged_tree=True)["balanced"] == 1
+    out, lse = _run(jf, case)
+    _check(case, out, lse, what=f"rw {rw} cus {cus}")
+
+
 def test_full_budgets_match_the_separate_tree_kernel_bit_for_bit(jf):
     case = W.make_paged_tree_case(25, [300, 17, 64], [24, 24, 24], N=24, Hq=8, Hkv=2, D=128, tree=("random", 6))
     out, lse = _run(jf, case)

@@ -563,7 +563,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     __shared__ float s_ml[KW][RB][2];
     __shared__ unsigned long long s_union[kAncWords];
     __shared__ int s_last;
-    __shared__ int s_plan[4];
+    __shared__ int s_plan[5];
     __shared__ int s_epi[6];
     __shared__ int s_tpages[kMaxTreePages];
 
@@ -587,10 +587,10 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
         //    so they start on the CUs that the short sequences free first, and end
         //    beside the heads instead of after them.
         // Units (sequence, piece, KV head) are ranked by piece size, largest first,
-        // and dealt round robin to the XCDs; a unit's nrb row blocks (which read the
-        // same K/V pages) run one after another on one XCD. Each XCD starts its
-        // workgroups in id order as its CUs free up, so it list-schedules its own
-        // longest-first share. Ids past the units are idle.
+        // and dealt round robin to the XCDs; a unit's row blocks that hold rows of
+        // the tree (which read the same K/V pages) run one after another on one XCD.
+        // Each XCD starts its workgroups in id order as its CUs free up, so it
+        // list-schedules its own longest-first share. Ids past the units are idle.
         if (w == 0) {
             const bool in = lane < a.B;
             const int Lm = in ? a.prefix_len[lane] : 0;
@@ -646,13 +646,13 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                 }
             }
             // units ranked before each group: larger keys first, ties by sequence,
-            // then group (without tails, one group per sequence: the shorter loop)
+            // then group (the loop index is uniform: lane j's values are read into
+            // scalar registers; without tails, one group per sequence: the shorter loop)
             int offa = 0, offb = 0;
             if (ht) {
-                const int nab = na | (nb << 16);
                 for (int j = 0; j < a.B; ++j) {
-                    const int kaj = __shfl(ka, j), kbj = __shfl(kb, j), nabj = __shfl(nab, j);
-                    const int naj = nabj & 0xffff, nbj = nabj >> 16;
+                    const int kaj = __builtin_amdgcn_readlane(ka, j), kbj = __builtin_amdgcn_readlane(kb, j);
+                    const int naj = __builtin_amdgcn_readlane(na, j), nbj = __builtin_amdgcn_readlane(nb, j);
                     offa += ((kaj > ka || (kaj == ka && j < lane)) ? naj : 0) +
                             ((kbj > ka || (kbj == ka && j < lane)) ? nbj : 0);
                     offb += ((kaj > kb || (kaj == kb && j <= lane)) ? naj : 0) +
@@ -660,21 +660,51 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                 }
             } else {
                 for (int j = 0; j < a.B; ++j) {
-                    const int kaj = __shfl(ka, j), naj = __shfl(na, j);
+                    const int kaj = __builtin_amdgcn_readlane(ka, j), naj = __builtin_amdgcn_readlane(na, j);
                     offa += (kaj > ka || (kaj == ka && j < lane)) ? naj : 0;
                 }
             }
-            const int slot = bid / kNumXcd;
-            const int u = (slot / a.nrb) * kNumXcd + bid % kNumXcd;
+            const int x = bid % kNumXcd, slot = bid / kNumXcd;
             const int loa = offa * a.Hkv, lob = offb * a.Hkv;
-            const bool mine_a = in && u >= loa && u < loa + na * a.Hkv;
-            const bool mine_b = in && nb > 0 && u >= lob && u < lob + nb * a.Hkv;
+            const int lv = in ? live : 0;
+            bool mine_a, mine_b;
+            int u, rbp;
+            if (__ballot(in && lv < a.nrb) == 0) {
+                // every row block holds rows: unit (slot / nrb) * 8 + x, row block slot % nrb
+                u = (slot / a.nrb) * kNumXcd + x;
+                rbp = slot % a.nrb;
+                mine_a = in && u >= loa && u < loa + na * a.Hkv;
+                mine_b = in && u >= lob && u < lob + nb * a.Hkv;
+            } else {
+                // Trees of ragged lengths: XCD x runs its units (u = x mod 8, in rank
+                // order) one after another, each with its live row blocks only, and
+                // workgroup id 8 k + x takes XCD x's k-th live slot. Row blocks past a
+                // sequence's tree get no workgroup, and ids past the last live slot are idle.
+                auto on_x = [&](int v) { return v > x ? (v - x + kNumXcd - 1) / kNumXcd : 0; };  // units u < v on x
+                const int wa = (on_x(loa + na * a.Hkv) - on_x(loa)) * lv;     // slots of each group on XCD x
+                const int wb = (on_x(lob + nb * a.Hkv) - on_x(lob)) * lv;
+                int sa = 0, sb = 0;                                            // slots of the groups ranked before
+                for (int j = 0; j < a.B; ++j) {
+                    const int loaj = __builtin_amdgcn_readlane(loa, j), lobj = __builtin_amdgcn_readlane(lob, j);
+                    const int waj = __builtin_amdgcn_readlane(wa, j), wbj = __builtin_amdgcn_readlane(wb, j);
+                    sa += (loaj < loa ? waj : 0) + (lobj < loa ? wbj : 0);
+                    sb += (loaj < lob ? waj : 0) + (lobj < lob ? wbj : 0);
+                }
+                mine_a = in && slot >= sa && slot < sa + wa;
+                mine_b = in && slot >= sb && slot < sb + wb;
+                const int lo = mine_a ? loa : lob;
+                const int local = slot - (mine_a ? sa : sb);
+                // the group's (local / lv)-th unit on XCD x, and its row block
+                u = lo + ((x - lo) % kNumXcd + kNumXcd) % kNumXcd + (local / max(lv, 1)) * kNumXcd;
+                rbp = local % max(lv, 1);
+            }
             if (mine_a || mine_b) {
                 const int lo = mine_a ? loa : lob;
                 s_plan[0] = lane;
                 s_plan[1] = (mine_a ? 0 : na) + (u - lo) / a.Hkv;
                 s_plan[2] = (u - lo) % a.Hkv;
                 s_plan[3] = pp;
+                s_plan[4] = rbp;
             }
             if (__ballot(mine_a || mine_b) == 0 && lane == 0) s_plan[0] = -1;
         }
@@ -684,7 +714,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
         s = __builtin_amdgcn_readfirstlane(s_plan[1]);
         kvh = __builtin_amdgcn_readfirstlane(s_plan[2]);
         pps = __builtin_amdgcn_readfirstlane(s_plan[3]);
-        rb = (bid / kNumXcd) % a.nrb;
+        rb = __builtin_amdgcn_readfirstlane(s_plan[4]);
     } else {
         // ids remapped so that one KV head's row blocks and splits share an XCD
         const int lid = xcd_remap(bid, nblk);
