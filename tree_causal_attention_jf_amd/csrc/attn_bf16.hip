@@ -361,8 +361,20 @@ __device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, 
         const int key = h2 * 32 + l32;
         return *reinterpret_cast<const bf16x8*>(kbuf + key * Gm::ROW_BYTES + (((2 * c + hf) ^ swz_k<D>(key)) << 4));
     };
+    // K operands one k-step ahead: the reads of step c + 1 are issued before the
+    // products of step c, so the LDS latency hides behind two products instead of
+    // standing between every pair (the asm keeps each step's products below the
+    // next step's reads; it reads the step's own operands, so the wait for them
+    // lands there and lets the newer reads stay in flight)
+    bf16x8 kf[DCH][2];
+    kf[0][0] = kfrag(0, 0);
+    kf[0][1] = kfrag(0, 1);
+    if constexpr (DCH > 1) {
+        kf[1][0] = kfrag(1, 0);
+        kf[1][1] = kfrag(1, 1);
+    }
+    asm volatile("" : "+v"(kf[0][0]), "+v"(kf[0][1])::"memory");
     {
-        const bf16x8 k0 = kfrag(0, 0), k1 = kfrag(0, 1);
         if (!src.tree && src.t0 + kKeyTile > src.limit) {
             const int nvalid = src.limit - src.t0 - 4 * hf;
             f32x16 b0, b1;
@@ -374,25 +386,29 @@ __device__ __forceinline__ void tile_product(RowState<D>* st, const char* kbuf, 
             }
             #pragma unroll
             for (int blk = 0; blk < RPW; ++blk) {
-                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[blk][0], b0, 0, 0, 0);
-                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[blk][0], b1, 0, 0, 0);
+                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][0], qreg[blk][0], b0, 0, 0, 0);
+                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][1], qreg[blk][0], b1, 0, 0, 0);
             }
         } else {
             #pragma unroll
             for (int blk = 0; blk < RPW; ++blk) {
-                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[blk][0], f32x16{}, 0, 0, 0);
-                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[blk][0], f32x16{}, 0, 0, 0);
+                sacc[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][0], qreg[blk][0], f32x16{}, 0, 0, 0);
+                sacc[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][1], qreg[blk][0], f32x16{}, 0, 0, 0);
             }
         }
     }
     #pragma unroll
     for (int c = 1; c < DCH; ++c) {
+        if (c + 1 < DCH) {
+            kf[c + 1][0] = kfrag(c + 1, 0);
+            kf[c + 1][1] = kfrag(c + 1, 1);
+        }
+        asm volatile("" : "+v"(kf[c][0]), "+v"(kf[c][1])::"memory");
         #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const bf16x8 kf = kfrag(c, h2);
             #pragma unroll
             for (int blk = 0; blk < RPW; ++blk)
-                sacc[blk][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[blk][c], sacc[blk][h2], 0, 0, 0);
+                sacc[blk][h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][h2], qreg[blk][c], sacc[blk][h2], 0, 0, 0);
         }
     }
     uint32_t pk[RPW][2][8];
