@@ -1201,8 +1201,8 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
         const int old = arrive(&a.counters[item]);
         s_last = (old == n_act - 1);
         if (s_last) {
+            acquire_agent();                   // before the reset: the fence waits for earlier stores
             reset_counter(&a.counters[item]);
-            acquire_agent();
         }
     }
     __syncthreads();

@@ -191,8 +191,11 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
 //           arrive(); no cache-wide write-back is needed, and many workgroups
 //           publishing at once do not serialize on one;
 //   reader: the thread that saw the last arrival calls acquire_agent()
-//           (invalidates this CU's L1 and this XCD's L2), tells the workgroup
-//           through LDS and a barrier, and the workgroup then loads normally.
+//           (invalidates this CU's L1 and this XCD's L2), and only then
+//           resets the counter (the fence waits for every store issued before
+//           it, a full round trip for a write-through one), tells the
+//           workgroup through LDS and a barrier, and the workgroup then loads
+//           normally.
 // Small results (8-byte argmax keys) are written and read with agent-scope
 // atomics, which bypass the non-coherent caches, and counted with arrive().
 __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }

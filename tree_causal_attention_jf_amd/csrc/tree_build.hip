@@ -911,8 +911,8 @@ __global__ __launch_bounds__(kBuildThreads) __attribute__((amdgpu_waves_per_eu(4
                 const int old = arrive(&a.seq_count[b]);
                 is_last = (old == expect - 1);
                 if (is_last) {
-                    reset_counter(&a.seq_count[b]);
                     acquire_agent();                            // the records are then read with plain loads
+                    reset_counter(&a.seq_count[b]);             // after the fence, which waits for earlier stores
                 }
             }
             s_last = is_last;
