@@ -39,7 +39,8 @@ Per-workload summaries in profiles/ (each file records its command):
     rocprofv3 --kernel-trace --stats -d D -o run --output-format csv -- python bench.py --only NAME --no-cpu-baseline
     python bench.py --summarize-stats D NAME
     rocprofv3 --pmc <MFMA_COUNTERS> -d D -o run --output-format csv -- python bench.py --only NAME --no-cpu-baseline --profile-reps 2
-    python bench.py --summarize-mfma D NAME KERNEL AVERAGE_US
+    rocprofv3 --pmc <LIMIT_COUNTERS> -d L -o run --output-format csv -- (the same bench.py command)
+    python bench.py --summarize-mfma D NAME KERNEL AVERAGE_US --limits L
 """
 
 from __future__ import annotations
@@ -88,6 +89,10 @@ def parse():
     ap.add_argument("--summarize-mfma", nargs=4, metavar=("PMC_DIR", "LABEL", "KERNEL", "DURATION_US"),
                     help="turn a rocprofv3 --pmc run of the MFMA counters into profiles/KERNEL_LABEL_mfma.txt "
                          "(KERNEL: a substring of the kernel name; DURATION_US: its average duration)")
+    ap.add_argument("--limits", default=None, metavar="PMC_DIR",
+                    help="with --summarize-mfma: a second rocprofv3 --pmc run of the LDS and VALU counters")
+    ap.add_argument("--limits-command", default="",
+                    help="with --limits: the profiler command line of that run")
     ap.add_argument("--command", default="",
                     help="with --summarize-*: the profiler command line to record in the summary")
     ap.add_argument("--profile-reps", type=int, default=0,
@@ -229,8 +234,13 @@ MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", 
                  "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
 
 
-def summarize_mfma(d, label, kernel, duration_us, command):
-    """profiles/<kernel>_<label>_mfma.txt from a rocprofv3 --pmc run of MFMA_COUNTERS."""
+# a second pass (the profiler takes at most 8 SQ counters per run): LDS read bytes, exponentials, VALU time
+LIMIT_COUNTERS = ("SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU")
+
+
+def summarize_mfma(d, label, kernel, duration_us, command, limits_dir=None, limits_command=""):
+    """profiles/<kernel>_<label>_mfma.txt from a rocprofv3 --pmc run of MFMA_COUNTERS (and, if given, a
+    second run of LIMIT_COUNTERS on the same workload)."""
     per = {}
     name = None
     for c in MFMA_COUNTERS:
@@ -260,6 +270,25 @@ def summarize_mfma(d, label, kernel, duration_us, command):
               f"# clock under load: busy cycles per XCD / the kernel's average duration ({duration_us} us, kernel trace)",
               f"clock_GHz: {clock:.2f}",
               f"mfma_busy_fraction_at_2400MHz: {mfma_cyc / (duration_us * 1e3 * 2.4):.3f}"]
+    if limits_dir:
+        lim = {}
+        for c in LIMIT_COUNTERS:
+            for n, v in read_counter_csv(limits_dir, c).items():
+                if kernel in n:
+                    lim.setdefault(c, []).extend(v)
+        lav = {k: sum(v) / len(v) for k, v in lim.items()}
+        cus = simds // 4
+        lds_bytes = lav["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64
+        lines += ["# second pass (same workload):",
+                  f"#   {limits_command}" if limits_command else "#   (command not given)"]
+        lines += [f"{k}: {lav[k]:.0f}" for k in sorted(lav)]
+        lines += ["# SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte units read from LDS, summed over all SIMDs",
+                  f"lds_read_bytes_per_dispatch: {lds_bytes:.0f}",
+                  f"lds_read_bytes_per_cu_per_gpu_cycle: {lds_bytes / cus / gpu_cyc:.1f}",
+                  f"lds_insts_per_mfma: {lav['SQ_INSTS_LDS'] / avg['SQ_INSTS_MFMA']:.2f}",
+                  f"exp_f32_per_mfma: {lav['SQ_INSTS_VALU_TRANS_F32'] / avg['SQ_INSTS_MFMA']:.2f}",
+                  "# SQ_ACTIVE_INST_VALU: quad-cycles that waves spend on VALU instructions, summed over waves",
+                  f"valu_wave_cycles_per_simd_cycle: {lav['SQ_ACTIVE_INST_VALU'] * 4 / simds / gpu_cyc:.3f}"]
     out = os.path.join(ROOT, "profiles", f"{short}_{label}_mfma.txt")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -855,7 +884,7 @@ def main():
         return
     if args.summarize_mfma:
         d, label, kernel, dur = args.summarize_mfma
-        summarize_mfma(d, label, kernel, float(dur), args.command)
+        summarize_mfma(d, label, kernel, float(dur), args.command, args.limits, args.limits_command)
         return
     global REPS_OVERRIDE
     REPS_OVERRIDE = args.profile_reps
