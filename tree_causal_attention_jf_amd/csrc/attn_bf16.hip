@@ -266,6 +266,44 @@ __device__ __forceinline__ void issue_round(const uint16_t* kp, const uint16_t* 
     }
 }
 
+// One prefix tile into LDS at `buf`, K transfers then V, with the tile's four
+// page ids in lanes 0..3 of `pages` (already checked): the same transfers as a
+// round's share for that tile, for a wave that requests its tile before the
+// page list is in LDS.
+template <int D>
+__device__ __forceinline__ void issue_tile_own_pages(const uint16_t* kp, const uint16_t* vp, int Hkv, int kvh,
+                                                     const TileSrc& src, int pages, const PageLanes<D>& pl,
+                                                     uint32_t buf, int lane) {
+    using Gm = Geo<D>;
+    constexpr int TPP = PageLanes<D>::TPP;
+    const int rsub = lane / Gm::CPR, pc = lane % Gm::CPR;
+    const bool full = src.t0 + kKeyTile <= src.limit;
+    #pragma unroll
+    for (int ii0 = 0; ii0 < Gm::XFER_PER_TILE; ii0 += TPP) {
+        const bool isv = ii0 >= Gm::KB_PER_TILE;
+        const int pq = (isv ? ii0 - Gm::KB_PER_TILE : ii0) / TPP;   // page of the tile
+        const uint32_t lds0 = buf + ii0 * 1024;
+        if (full) {
+            const int page = __builtin_amdgcn_readlane(pages, pq);
+            const uint16_t* base = uniform_ptr((isv ? vp : kp) + ((long)page * Hkv + kvh) * (kPage * D));
+            #pragma unroll
+            for (int kb = 0; kb < TPP; ++kb)
+                dma16_s(__builtin_amdgcn_readfirstlane(lds0 + kb * 1024), base, isv ? pl.v[kb] : pl.k[kb]);
+        } else {
+            #pragma unroll
+            for (int kb = 0; kb < TPP; ++kb) {
+                const int row = pq * kPage + kb * Gm::ROWS_PER_KB + rsub;     // key within the tile
+                const int c = pc ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+                int t = src.t0 + row;
+                if (t >= src.limit) t = src.t0;
+                const int page = __shfl(pages, (t >> 4) - (src.t0 >> 4));
+                const uint16_t* gp = (isv ? vp : kp) + (((long)page * Hkv + kvh) * kPage + (t & 15)) * D + c * 8;
+                dma16(__builtin_amdgcn_readfirstlane(lds0 + kb * 1024), gp);
+            }
+        }
+    }
+}
+
 // The tree tiles of a workgroup that runs the tree alone (its own split) in a
 // one-round ring, requested before anything else: their addresses depend on
 // no loaded value (the tree's K/V are the separate [B, N, Hkv, D] arrays). Wave
@@ -775,6 +813,13 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     // an absent array replaced by prefix_len, a valid address) and its value is
     // selected where it is used: the compiler then counts the loads exactly, and a
     // wait for one of them never also waits for every load issued after it.
+    // (one-round rings with one tile per wave: this wave's four page ids of the
+    // split's first round, in lanes 0..3, first of all)
+    int own_pages = 0;
+    if constexpr (RING_R == 1 && RW == 1)
+        own_pages = *(p_avail > 0 ? a.block_table + (long)b * a.max_pages + p_begin +
+                                        min(4 * kw + min(lane, 3), p_avail - 1)
+                                  : a.prefix_len + b);
     int L = a.prefix_len[b];
     const int nb_raw = *(a.tree_len ? a.tree_len + b : a.prefix_len + b);
     // when this launch builds the ancestor words itself: the parent of node `lane`
@@ -847,6 +892,31 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
     const int p_end = tree_wg ? 0 : min(npages, p_begin + pps);
     const int tok_begin = p_begin * kPage;
     const int tok_end = tree_wg ? 0 : min(L, p_end * kPage);
+    // A prefix split of a one-round ring with one tile per wave (and no tree tiles)
+    // requests its round here, once its page ids and lengths have landed, so that
+    // the tiles move while the rest of the set-up runs. Every set-up load but Q's is
+    // waited for first: the compiler's own waits do not count the transfers, so a
+    // later wait for one of those loads would also wait for the round.
+    bool early_pre = false;
+    if constexpr (RING_R == 1 && RW == 1) {
+        early_pre = !has_tree && !a.paged_tree && p_end > p_begin;
+        if (early_pre) {
+            asm volatile("" ::"v"(par_raw), "v"(own_pages));
+            #pragma unroll
+            for (int k = 0; k < PPT; ++k) asm volatile("" ::"v"(pid[k]));
+            #pragma unroll
+            for (int k = 0; k < kAncWords; ++k) asm volatile("" ::"v"(ancw[0][k]));
+            const int n_pre0 = (tok_end - tok_begin + kKeyTile - 1) / kKeyTile;
+            if (kw < n_pre0) {                          // wave-uniform
+                const int pv = (own_pages < 0 || own_pages >= a.num_pages) ? 0 : own_pages;
+                const TileSrc src{false, tok_begin + kw * kKeyTile, tok_end};
+                issue_tile_own_pages<D>(a.kp, a.vp, a.Hkv, kvh, src, pv, page_lanes<D>(lane),
+                                        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)ring) +
+                                            kw * Gm::BUF_BYTES,
+                                        lane);
+            }
+        }
+    }
     if (a.parent_sets && has_tree) {
         // the ancestor words come from the parent array (the loads above read a
         // buffer this launch writes, and are discarded): pointer doubling across the
@@ -1022,7 +1092,7 @@ __device__ __forceinline__ void tree_attn_bf16_body(const AttnArgs& a, const uns
                                     s_tpages, tree_tok0);
         } else {
             __syncthreads();      // every wave is done with the previous round
-            if (!(early_tree && r == 0))
+            if (!((early_tree || early_pre) && r == 0))
                 issue_round<D, DPR>(g_kp, g_vp, g_kt, g_vt, N, Hkv, tile_src, r * KW, n_tiles, b, kvh, s_pages, pl,
                                     ring0, w * DPR, lane, s_tpages, tree_tok0);
             wait_vm<0>();
