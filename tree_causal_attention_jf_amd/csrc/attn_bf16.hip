@@ -28,10 +28,11 @@
 //     head's row blocks and splits land on one XCD and share its L2. Batches of
 //     2..64 sequences: each workgroup plans from the prefix lengths themselves
 //     (the host knows only the longest). A sequence with more than 1.5x the
-//     mean work per CU is cut into ceil(work / mean) pieces; units (sequence,
-//     piece, KV head) are ranked by piece size and dealt round robin to the
-//     XCDs, a unit's row blocks together, so that every XCD list-schedules its
-//     own longest-first share.
+//     mean work per CU is cut into ceil(work / mean) pieces, or, when that fits
+//     one round of CUs but the rest would not, into a head and a tail; units
+//     (sequence, piece, KV head) are ranked by piece size and dealt round robin
+//     to the XCDs, a unit's row blocks together (only those that hold rows of
+//     the tree), so that every XCD list-schedules its own longest-first share.
 //
 // Data movement: 64-key tiles of K and V go from HBM straight into a 4-tile
 // LDS ring with global_load_lds_dwordx4 (16 bytes per lane, no staging
@@ -39,6 +40,8 @@
 // counts its own transfers with vmcnt and a barrier publishes a round to all
 // waves. Rows are stored as they are in the cache (key-major), 16-byte chunks
 // XOR-swizzled per key so that the matrix-operand reads are bank-conflict free.
+// A one-round ring's prefix split (the few-row plans of budget-16 steps) requests
+// its round as soon as its page ids have landed, while the rest of the set-up runs.
 //
 // Per tile, per wave (32 query rows):
 //   S^T[key, row] = K_tile Q^T     (A = K rows via ds_read_b128, B = Q in registers)
