@@ -501,6 +501,45 @@ def test_attention_bad_inputs_give_nan_rows(jf):
     assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
 
 
+@pytest.mark.parametrize("L", [1000, 2048, 7])
+def test_attention_one_sequence_table_wider_than_prefix(jf, L):
+    # one sequence in the few-row plan (each wave requests its first tile as soon as
+    # its page ids land): the host's longest prefix (2048) is above the sequence's own,
+    # and the block table is wider than the prefix, its entries past the prefix's
+    # pages invalid; those entries are never used, and the ragged last tile reads only
+    # its valid keys
+    wl = W.make_workload("c1_chain16", 21, with_accept=False, B=1, N=16, prefix=("list", [L]), Hq=32, Hkv=8,
+                         tree=("chain",))
+    d = to_dev(wl)
+    pages = d["block_table"].shape[1]
+    wide = torch.full((1, 128), -1, dtype=torch.int32, device=DEV)
+    wide[:, :pages] = d["block_table"]
+    anc, _, _ = jf.build_ancestor_mask(d["parent"])
+    out, lse = jf.tree_attention(d["q"], d["k_pages"], d["v_pages"], wide, d["prefix_len"], d["k_tree"],
+                                 d["v_tree"], anc, sm_scale=wl.sm_scale, max_prefix_len=2048, return_lse=True)
+    torch.cuda.synchronize()
+    ref, lref = _oracle_full(wl)
+    check_bf16(out, ref, lse, lref, f"one sequence, prefix {L}, table of 128 pages")
+
+
+def test_attention_one_sequence_bad_page_in_first_round(jf):
+    # an invalid page id inside a split's first round, in the few-row plan: the
+    # sequence's rows are NaN (the tile is requested from a clamped id before the page
+    # checks run, and the checks still flag it)
+    wl = W.make_workload("c1_chain16", 22, with_accept=False, B=1, N=16, prefix=("list", [2048]), Hq=32, Hkv=8,
+                         tree=("chain",))
+    d = to_dev(wl)
+    for bad in (-3, 1 << 30):
+        d2 = dict(d)
+        d2["block_table"] = d["block_table"].clone()
+        d2["block_table"][0, 21] = bad                   # split 1 (pages 16..31), its second tile
+        out, lse = run_attention(jf, wl, d2)
+        assert torch.isnan(out.float()).all() and torch.isnan(lse).all(), bad
+    out, lse = run_attention(jf, wl, d)
+    ref, lref = _oracle_full(wl)
+    check_bf16(out, ref, lse, lref, "one sequence, valid table")
+
+
 def test_graph_replay_matches_eager(jf):
     wl = W.make_workload("c1_chain16", 3, with_accept=True)
     d = to_dev(wl)
